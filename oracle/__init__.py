@@ -1,0 +1,205 @@
+"""Plain FP64 CPU oracle for the paged BF16 KV-cache decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+(``paged_kv_cache_172_amd``) never imports it, and the two share no code.
+
+The arithmetic lives in ``pkv_oracle.c`` (plain C, FP64, single-threaded,
+built without FMA contraction); this module only builds it with gcc and
+marshals numpy arrays into it.  Every routine follows the plain definition of
+what the pages describe (the header comment of ``pkv_oracle.c`` names the
+passages and the readings taken where the pages are silent).
+
+``Oracle(path)`` wraps one build of the library; the module-level functions
+use the default build.  Tests also build deliberately mutated copies of the
+source (on the CPU) to show that the pins catch plausible mistakes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "pkv_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
+
+NUM_Q_HEADS = 32
+NUM_KV_HEADS = 8
+HEAD_DIM = 64
+PAGE_TOKENS = 16
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle source file into a shared library with gcc."""
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", out + ".tmp", src, "-lm"], check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build() -> str:
+    """Compile the default oracle build (FP64, no FMA contraction)."""
+    return compile_source(SOURCE, LIB_PATH)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _req(a, dtype, name):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"{name} must be a C-contiguous numpy array of {np.dtype(dtype)}")
+    return a
+
+
+class PoolView:
+    """Host pool: K and V base arrays (may be views of one buffer) with element
+    strides per page, per KV head and per slot."""
+
+    def __init__(self, k, v, num_pages, page_stride, head_stride, slot_stride):
+        self.k = k
+        self.v = v
+        self.num_pages = int(num_pages)
+        self.page_stride = int(page_stride)
+        self.head_stride = int(head_stride)
+        self.slot_stride = int(slot_stride)
+
+    @classmethod
+    def from_pages(cls, pages: np.ndarray) -> "PoolView":
+        """pages: uint16 [num_pages][2][8][16][64] (K half, then V half)."""
+        _req(pages, np.uint16, "pages")
+        flat = pages.reshape(-1)
+        half = NUM_KV_HEADS * PAGE_TOKENS * HEAD_DIM
+        return cls(flat, flat[half:], pages.shape[0], 2 * half, PAGE_TOKENS * HEAD_DIM,
+                   HEAD_DIM)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact FP64 values of BF16 bit patterns (bit placement, no arithmetic)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+class Oracle:
+    def __init__(self, path: str = LIB_PATH):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.pkv_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.pkv_oracle_bf16_to_f64.restype = dbl
+        lib.pkv_oracle_bf16_round.argtypes = [dbl]
+        lib.pkv_oracle_bf16_round.restype = ctypes.c_uint16
+        lib.pkv_oracle_rope_table.argtypes = [dbl, i32, P, P]
+        lib.pkv_oracle_rope_table.restype = ctypes.c_int
+        lib.pkv_oracle_rope_rotate_f64.argtypes = [P, P, P, P]
+        lib.pkv_oracle_rope_rotate_f64.restype = None
+        lib.pkv_oracle_locate.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.pkv_oracle_locate.restype = ctypes.c_int
+        lib.pkv_oracle_num_pages.argtypes = [i32]
+        lib.pkv_oracle_num_pages.restype = i32
+        lib.pkv_oracle_append.argtypes = [
+            P, P, i64, i64, i64, i64, P, i64, P, i32, P, i64, P, i64, P, i64, P, P, i32]
+        lib.pkv_oracle_append.restype = ctypes.c_int
+        lib.pkv_oracle_attn.argtypes = [
+            P, P, i64, i64, i64, i64, P, i64, P, i32, P, i64, dbl, P, i64, P, i64]
+        lib.pkv_oracle_attn.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    # ------------------------------------------------------------- BF16 --
+    def bf16_round(self, y: float) -> int:
+        """Nearest BF16 bit pattern to the FP64 value y (ties to even)."""
+        return int(self.lib.pkv_oracle_bf16_round(float(y)))
+
+    def bf16_value(self, bits: int) -> float:
+        return float(self.lib.pkv_oracle_bf16_to_f64(int(bits)))
+
+    def bf16_round_array(self, y) -> np.ndarray:
+        f = self.lib.pkv_oracle_bf16_round
+        flat = np.asarray(y, dtype=np.float64).ravel()
+        out = np.fromiter((f(float(x)) for x in flat), dtype=np.uint16, count=flat.size)
+        return out.reshape(np.shape(y))
+
+    # ------------------------------------------------------------- RoPE --
+    def rope_table(self, theta: float = 500000.0, max_pos: int = 2048):
+        """FP32 cos/sin tables [max_pos][32]."""
+        cos = np.empty((max_pos, HEAD_DIM // 2), np.float32)
+        sin = np.empty((max_pos, HEAD_DIM // 2), np.float32)
+        if self.lib.pkv_oracle_rope_table(float(theta), int(max_pos), _ptr(cos), _ptr(sin)):
+            raise ValueError("rope_table: invalid arguments")
+        return cos, sin
+
+    def rope_rotate_f64(self, x, cos_row, sin_row) -> np.ndarray:
+        """Rotate one 64-wide FP64 vector with FP32 table rows, no rounding."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        c = np.ascontiguousarray(cos_row, dtype=np.float32)
+        s = np.ascontiguousarray(sin_row, dtype=np.float32)
+        y = np.empty(HEAD_DIM, np.float64)
+        self.lib.pkv_oracle_rope_rotate_f64(_ptr(x), _ptr(c), _ptr(s), _ptr(y))
+        return y
+
+    # --------------------------------------------------------- indexing --
+    def locate(self, ctx: int):
+        """(logical page, slot) of the token that makes the context ctx long."""
+        j, t = ctypes.c_int32(), ctypes.c_int32()
+        if self.lib.pkv_oracle_locate(int(ctx), ctypes.byref(j), ctypes.byref(t)) != 0:
+            raise ValueError("ctx must be >= 1")
+        return j.value, t.value
+
+    def num_pages(self, ctx: int) -> int:
+        return int(self.lib.pkv_oracle_num_pages(int(ctx)))
+
+    # ------------------------------------------------ append / attention --
+    def append(self, pool: PoolView, block_table, ctx, q, k, v, rope_cos, rope_sin) -> None:
+        """In place: rotates q rows and writes K'/V into the pool.
+
+        block_table int32 [B][bt_stride]; ctx int32 [B]; q uint16 [B][q_stride];
+        k, v uint16 [B][stride]; rope tables float32 [max_pos][32]."""
+        _req(block_table, np.int32, "block_table")
+        _req(ctx, np.int32, "ctx")
+        for a, n in ((q, "q"), (k, "k"), (v, "v")):
+            _req(a, np.uint16, n)
+        _req(rope_cos, np.float32, "rope_cos")
+        _req(rope_sin, np.float32, "rope_sin")
+        rc = self.lib.pkv_oracle_append(
+            _ptr(pool.k), _ptr(pool.v), pool.num_pages, pool.page_stride, pool.head_stride,
+            pool.slot_stride, _ptr(block_table), block_table.shape[1], _ptr(ctx),
+            ctx.shape[0], _ptr(q), q.shape[1], _ptr(k), k.shape[1], _ptr(v), v.shape[1],
+            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0])
+        if rc != 0:
+            raise ValueError(f"oracle append failed ({rc})")
+
+    def attn(self, pool: PoolView, block_table, ctx, q, scale: float, want64: bool = False):
+        """FP32 output [B][32*64] (and the FP64 output when want64)."""
+        _req(block_table, np.int32, "block_table")
+        _req(ctx, np.int32, "ctx")
+        _req(q, np.uint16, "q")
+        B = ctx.shape[0]
+        row = NUM_Q_HEADS * HEAD_DIM
+        out32 = np.zeros((B, row), np.float32)
+        out64 = np.zeros((B, row), np.float64) if want64 else None
+        rc = self.lib.pkv_oracle_attn(
+            _ptr(pool.k), _ptr(pool.v), pool.num_pages, pool.page_stride, pool.head_stride,
+            pool.slot_stride, _ptr(block_table), block_table.shape[1], _ptr(ctx), B,
+            _ptr(q), q.shape[1], float(scale), _ptr(out64), row, _ptr(out32), row)
+        if rc != 0:
+            raise ValueError(f"oracle attention failed ({rc})")
+        return (out32, out64) if want64 else out32
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The default oracle build, compiled on first use if missing or stale."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
