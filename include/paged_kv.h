@@ -1,0 +1,204 @@
+/*
+ * paged_kv.h -- C ABI of libpagedkv.so: the decode step over a paged BF16 KV
+ * cache on an AMD Instinct MI355X (gfx950).
+ *
+ * Passages this library implements:
+ *   [HN-pool]   "Hours of YouTube and 85 handtyped pages of notes on LLM
+ *               Inference - Start here" (hackernews.jp translation of the
+ *               project README), section "これまでの進捗" (progress so far),
+ *               bullet on the shared BF16 KV page pool: one block table per
+ *               sequence and layer, each physical page holds K and V of 16
+ *               tokens, decode adds one new token at its absolute RoPE
+ *               position.
+ *   [HN-attn]   same page and section, bullet on paged decode attention with
+ *               an FP32 online softmax: every query head streams its own
+ *               sequence's cached pages and accumulates weighted V, without
+ *               gathering a contiguous prefix and without storing scores.
+ *   [HN-batch]  same page and section, bullet on batch decode: runtime-sized
+ *               buffers, packed projections, a separate page mapping and
+ *               attention length per sequence; the request count does not
+ *               grow the pool.
+ *   [HN-scope]  same page, section "現在のスコープ" (current scope): model
+ *               dimensions and the 2,048-token context are fixed; a request
+ *               that cannot fit is refused with a clear error.
+ *   [TV-decode] "Tiny-vLLMでゼロから構築する高性能LLM推論エンジン"
+ *               (agentlenshq.com), section "Prefill vs. Decode": decode is
+ *               bound by memory bandwidth; section "GPUメモリ管理": allocate
+ *               big buffers up front and reuse them.
+ *
+ * Geometry is fixed to the Llama-3.2-1B attention shape the pages use
+ * ([HN-scope]): 32 query heads, 8 KV heads (query head h reads KV head h/4),
+ * head dimension 64, 16 tokens per page, contexts of at most 2,048 tokens.
+ *
+ * Conventions for every call:
+ *   - BF16 values travel as raw uint16_t bit patterns.
+ *   - Pointers marked (device) are device memory of the current HIP device;
+ *     (host) pointers are host memory.  All buffers belong to the caller;
+ *     no call allocates or frees memory, and the library keeps no state
+ *     besides a per-thread copy of the last HIP error text.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; calls that share
+ *     buffers must be ordered by the caller (same stream, or events).
+ *   - Element strides count elements of the buffer's own type.
+ *   - Every argument check happens on the host before any HIP call, so a
+ *     non-zero status means nothing was enqueued.  Values that live in
+ *     device memory (context lengths, table entries) are preconditions the
+ *     library does not check; breaking one is undefined behaviour.
+ *   - The calls are reentrant and thread-safe.
+ */
+#ifndef PAGED_KV_H_
+#define PAGED_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_NUM_Q_HEADS 32
+#define PKV_NUM_KV_HEADS 8
+#define PKV_HEAD_DIM 64
+#define PKV_PAGE_TOKENS 16
+#define PKV_MAX_CONTEXT 2048
+
+/* Status codes. */
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1)   /* null pointer, negative count or stride, range error */
+#define PKV_ERR_ALIGNMENT (-2)     /* pointer not 16-byte aligned or stride not a multiple of 16 bytes */
+#define PKV_ERR_WORKSPACE (-3)     /* workspace smaller than paged_decode_attn_workspace_size() */
+#define PKV_ERR_UNSUPPORTED (-4)   /* reserved for geometries other than the fixed one */
+#define PKV_ERR_HIP (-5)           /* a HIP launch failed; text via paged_kv_status_string */
+
+/*
+ * The shared page pool ([HN-pool]).  Element (page p, KV head g, slot t,
+ * dim d) of K lives at k_pool[p*page_stride + g*head_stride + t*slot_stride + d],
+ * and of V at the same offset from v_pool.  Dims of one slot are contiguous.
+ * Default layout: page = [K | V][8 heads][16 slots][64 dims] BF16 = 32 KiB,
+ * i.e. page_stride 16384, head_stride 1024, slot_stride 64 and
+ * v_pool = k_pool + 8192.  k_pool and v_pool: (device), 16-byte aligned;
+ * the three strides must be positive multiples of 8 elements.
+ */
+typedef struct paged_kv_pool {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int64_t num_pages;
+    int64_t page_stride;
+    int64_t head_stride;
+    int64_t slot_stride;
+} paged_kv_pool;
+
+/*
+ * RoPE table for the append ([HN-pool]: the new token is rotated at its
+ * absolute position).  Fills cos_out/sin_out (host, [max_pos][32] FP32,
+ * row-major) with cos and sin of pos * theta^(-2i/64), computed in FP64 and
+ * rounded once to FP32.  Llama 3.2 uses theta = 500000.  Upload the table
+ * once and pass it to every paged_kv_append call.
+ * Errors: INVALID_ARG for null outputs, max_pos < 1 or theta <= 0.
+ */
+int paged_kv_rope_table(double theta, int32_t max_pos, float* cos_out, float* sin_out);
+
+/*
+ * Decode append ([HN-pool], [HN-batch]).  For each sequence s < num_seqs with
+ * n = context_lens[s] >= 1 (the length AFTER this append), the new token sits
+ * at position pos = n-1:
+ *   - the 32 heads of q[s] and the 8 heads of k_new[s] are rotated by the
+ *     table row pos (pairs (i, i+32), i < 32), each result rounded once to
+ *     BF16 with ties to even; q[s] is overwritten in place;
+ *   - rotated K and unchanged V of KV head g go to page
+ *     block_table[s*bt_stride + pos/16], slot pos%16.
+ * Sequences with n <= 0 are skipped (nothing written).
+ *   pool          (host struct, device arrays) the page pool
+ *   block_table   (device) int32 [num_seqs][bt_stride], this layer's tables
+ *   context_lens  (device) int32 [num_seqs]
+ *   q             (device) BF16 [num_seqs][q_stride], heads at h*64, >= 2048 per row
+ *   k_new, v_new  (device) BF16 [num_seqs][k_stride / v_stride], heads at g*64
+ *   rope_cos/sin  (device) FP32 [max_pos][32] from paged_kv_rope_table
+ * q, k_new and v_new may be slices of one packed QKV buffer.
+ * Preconditions (unchecked): 1 <= n <= max_pos, the table entry for pos is a
+ * page < num_pages, and no two sequences write the same (page, slot).
+ * Errors: INVALID_ARG (null pointer, num_seqs < 0, bt_stride < 1, a stride
+ * below its row width, max_pos < 1), ALIGNMENT, HIP.  num_seqs == 0: no-op.
+ */
+int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs, uint16_t* q, int64_t q_stride,
+                    const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                    int64_t v_stride, const float* rope_cos, const float* rope_sin,
+                    int32_t max_pos, void* stream);
+
+/*
+ * Split plan of the decode attention.  The context of every sequence is cut
+ * into chunks of whole pages; chunk c of a sequence covers logical pages
+ * [c*P, (c+1)*P) where P = ceil(ceil(max_context_len/16) / S).  S depends only
+ * on (num_seqs, max_context_len), so results are bitwise reproducible and
+ * independent of where pages sit in the pool.  Returns S >= 1, or 0 for
+ * arguments outside num_seqs >= 1, 1 <= max_context_len <= 2048.
+ */
+int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
+
+/*
+ * Bytes of device workspace paged_decode_attn needs for this plan: 0 when
+ * S == 1, else S * num_seqs * 32 * 66 * 4 (per chunk and query head: 64
+ * accumulator values, a running maximum and a running sum, FP32).
+ * Returns 0 for arguments outside the ranges above.
+ */
+size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_len);
+
+/*
+ * Paged decode attention ([HN-attn], [HN-batch], [TV-decode]).  For each
+ * sequence s, query head h and n = context_lens[s]:
+ *   out[s][h*64 + d] = sum_{t<n} softmax_t(scale * q[s][h].K[t][h/4]) V[t][h/4][d]
+ * over the logical token order t, where token t is read from page
+ * block_table[s*bt_stride + t/16], slot t%16.  FP32 online softmax over BF16
+ * inputs; the context is cut into S chunks (paged_decode_attn_num_splits)
+ * whose partial results are merged with the log-sum-exp rule.  Rows with
+ * n <= 0 are written as zeros.  Tokens at or past n, pages no table entry
+ * below ceil(n/16) names, and table entries at or past ceil(n/16) are
+ * never read.
+ *   max_context_len  host-known upper bound of every context_lens[s] (drives the plan)
+ *   q                (device) BF16 [num_seqs][q_stride], already rotated
+ *   out              (device) FP32 [num_seqs][out_stride], >= 2048 per row
+ *   workspace        (device) >= paged_decode_attn_workspace_size() bytes,
+ *                    16-byte aligned; may be NULL when that size is 0.
+ *                    Calls running concurrently need separate workspaces.
+ * Preconditions (unchecked): 0 <= context_lens[s] <= max_context_len and the
+ * table entries below ceil(n/16) are pages < num_pages.
+ * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
+ * [1, min(2048, 16*bt_stride)], non-finite scale, a stride below its row
+ * width), ALIGNMENT (out_stride must be a multiple of 4), WORKSPACE, HIP.
+ * num_seqs == 0: no-op.
+ */
+int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      const uint16_t* q, int64_t q_stride, float scale, float* out,
+                      int64_t out_stride, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of paged_decode_attn as separate calls, for callers that
+ * time or schedule them apart.  Enqueuing paged_decode_attn_split then
+ * paged_decode_attn_combine on one stream with the same arguments is exactly
+ * paged_decode_attn.  The split phase streams the pages and writes one
+ * partial (maximum, sum, accumulator) per chunk into the workspace -- or,
+ * when S == 1, the final rows into out.  The combine phase merges the
+ * partials into out; when S == 1 it enqueues nothing.  Same arguments,
+ * checks and errors as paged_decode_attn.
+ */
+int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
+                            int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, const uint16_t* q, int64_t q_stride,
+                            float scale, float* out, int64_t out_stride, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, float* out, int64_t out_stride,
+                              const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for a status code; for PKV_ERR_HIP it includes the last HIP error
+ * text seen by this thread.  The pointer stays valid until the next call
+ * from the same thread. */
+const char* paged_kv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H_ */

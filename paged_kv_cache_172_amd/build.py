@@ -1,0 +1,72 @@
+"""Build libpagedkv.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_cache_172_amd.build [--save-temps DIR] [-D NAME=VALUE ...]
+
+Compiles csrc/kernels.hip (device code + launches) and csrc/api.cpp (the C
+ABI) into paged_kv_cache_172_amd/libpagedkv.so.  Packed FP32 instructions are
+disabled for device code (-target-feature -packed-fp32-ops): the kernels use
+plain FP32 VALU, DPP and v_dot2_f32_bf16 only.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpagedkv.so")
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libpagedkv.so)")
+
+
+def build(out: str = LIB, defines=(), save_temps: str | None = None, verbose=False) -> str:
+    cmd = [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        "-I", INCLUDE, "-I", CSRC,
+    ]
+    cmd += [f"-D{d}" for d in defines]
+    if save_temps:
+        save_temps = os.path.abspath(save_temps)
+        os.makedirs(save_temps, exist_ok=True)
+        cmd += ["-save-temps=obj", "-o", os.path.join(save_temps, "libpagedkv.so")]
+    cmd += SOURCES
+    tmp = out + ".tmp"
+    if not save_temps:
+        cmd += ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True,
+                       cwd=save_temps if save_temps else None)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr[-6000:]}")
+    if save_temps:
+        shutil.copy(os.path.join(save_temps, "libpagedkv.so"), tmp)
+    os.replace(tmp, out)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--save-temps", default=None, help="keep intermediate files (ISA) in this directory")
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("-v", action="store_true")
+    a = ap.parse_args()
+    print(build(a.out, a.defines, a.save_temps, a.v))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+// C ABI of libpagedkv.so (declared in include/paged_kv.h): host-side argument
+// checks, the split planner, and the kernel launches.  Every check runs
+// before any HIP call, so a rejected call enqueues nothing; invalid requests
+// get a clear status instead of undefined device behaviour ("Hours of YouTube
+// and 85 handtyped pages of notes on LLM Inference - Start here", section
+// "現在のスコープ": a request that cannot fit is refused with a clear error).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+#include "paged_kv.h"
+
+namespace pkv {
+
+// Split planner.  A decode batch has num_seqs * 8 (sequence, KV head) units;
+// each chunk of a unit is one wavefront.  The plan aims for about
+// kTargetWaves wavefronts (a few per SIMD of a 256-CU part) so that small
+// batches still fill the chip, and never cuts chunks below kMinPagesPerSplit
+// pages.  It depends only on (num_seqs, max_context_len).
+#ifndef PKV_TARGET_WAVES
+#define PKV_TARGET_WAVES 3072
+#endif
+#ifndef PKV_MIN_PAGES_PER_SPLIT
+#define PKV_MIN_PAGES_PER_SPLIT 4
+#endif
+constexpr int64_t kTargetWaves = PKV_TARGET_WAVES;
+constexpr int32_t kMinPagesPerSplit = PKV_MIN_PAGES_PER_SPLIT;
+
+static bool plan_args_ok(int32_t num_seqs, int32_t max_context_len) {
+    return num_seqs >= 1 && max_context_len >= 1 && max_context_len <= kMaxContext;
+}
+
+Plan make_plan(int32_t num_seqs, int32_t max_context_len) {
+    const int32_t max_pages = (max_context_len + kPageTokens - 1) / kPageTokens;
+    const int64_t units = (int64_t)num_seqs * kKVHeads;
+    int64_t s = (kTargetWaves + units - 1) / units;
+    const int32_t s_cap = (max_pages + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+    if (s > s_cap) s = s_cap;
+    if (s < 1) s = 1;
+    const int32_t pps = (int32_t)((max_pages + s - 1) / s);
+    const int32_t splits = (max_pages + pps - 1) / pps;
+    return Plan{splits, pps};
+}
+
+size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len) {
+    const Plan plan = make_plan(num_seqs, max_context_len);
+    if (plan.splits <= 1) return 0;
+    return (size_t)plan.splits * (size_t)num_seqs * kQHeads * kPartialFloats * sizeof(float);
+}
+
+}  // namespace pkv
+
+namespace {
+
+thread_local char g_status_text[256];
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return PKV_OK;
+    snprintf(g_status_text, sizeof g_status_text, "HIP error: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_pool(const paged_kv_pool* pool) {
+    if (!pool || !pool->k_pool || !pool->v_pool) return PKV_ERR_INVALID_ARG;
+    if (pool->num_pages < 1 || pool->page_stride < 1 || pool->head_stride < 1 ||
+        pool->slot_stride < pkv::kHeadDim)
+        return PKV_ERR_INVALID_ARG;
+    if (pool->num_pages > INT32_MAX) return PKV_ERR_INVALID_ARG;  // page ids are int32
+    if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool)) return PKV_ERR_ALIGNMENT;
+    if (pool->page_stride % 8 || pool->head_stride % 8 || pool->slot_stride % 8)
+        return PKV_ERR_ALIGNMENT;
+    return PKV_OK;
+}
+
+struct AttnCheck {
+    int status;
+    pkv::AttnParams params;
+};
+
+AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                     const uint16_t* q, int64_t q_stride, float scale, float* out,
+                     int64_t out_stride, void* workspace, size_t workspace_bytes) {
+    AttnCheck r{};
+    r.status = PKV_ERR_INVALID_ARG;
+    if (num_seqs < 0) return r;
+    if (num_seqs == 0) {
+        r.status = PKV_OK;
+        return r;
+    }
+    int st = check_pool(pool);
+    if (st != PKV_OK) {
+        r.status = st;
+        return r;
+    }
+    if (!block_table || !context_lens || !q || !out) return r;
+    if (bt_stride < 1 || max_context_len < 1 || max_context_len > pkv::kMaxContext) return r;
+    if ((int64_t)max_context_len > bt_stride * pkv::kPageTokens) return r;
+    if (!isfinite(scale)) return r;
+    if (q_stride < pkv::kQHeads * pkv::kHeadDim || out_stride < pkv::kQHeads * pkv::kHeadDim)
+        return r;
+    if (!aligned16(q) || !aligned16(out) || q_stride % 8 || out_stride % 4) {
+        r.status = PKV_ERR_ALIGNMENT;
+        return r;
+    }
+    const size_t need = pkv::workspace_bytes(num_seqs, max_context_len);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) {
+            r.status = PKV_ERR_WORKSPACE;
+            return r;
+        }
+        if (!aligned16(workspace)) {
+            r.status = PKV_ERR_ALIGNMENT;
+            return r;
+        }
+    }
+    pkv::AttnParams& p = r.params;
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.num_pages = pool->num_pages;
+    p.page_stride = pool->page_stride;
+    p.head_stride = pool->head_stride;
+    p.slot_stride = pool->slot_stride;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.max_context_len = max_context_len;
+    p.q = q;
+    p.q_stride = q_stride;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale / ln 2
+    p.plan = pkv::make_plan(num_seqs, max_context_len);
+    p.out = out;
+    p.out_stride = out_stride;
+    if (need > 0) {
+        const size_t acc_bytes =
+            (size_t)p.plan.splits * num_seqs * pkv::kQHeads * pkv::kHeadDim * sizeof(float);
+        p.ws_acc = static_cast<float*>(workspace);
+        p.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + acc_bytes);
+    }
+    r.status = PKV_OK;
+    return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_rope_table(double theta, int32_t max_pos, float* cos_out, float* sin_out) {
+    if (!cos_out || !sin_out || max_pos < 1 || !(theta > 0.0) || !isfinite(theta))
+        return PKV_ERR_INVALID_ARG;
+    for (int32_t pos = 0; pos < max_pos; ++pos) {
+        for (int i = 0; i < pkv::kHeadDim / 2; ++i) {
+            // angle = pos * theta^(-2i/64), FP64, then one rounding to FP32
+            const double freq = pow(theta, -(double)(2 * i) / (double)pkv::kHeadDim);
+            const double angle = (double)pos * freq;
+            cos_out[(int64_t)pos * 32 + i] = (float)cos(angle);
+            sin_out[(int64_t)pos * 32 + i] = (float)sin(angle);
+        }
+    }
+    return PKV_OK;
+}
+
+int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                    const int32_t* context_lens, int32_t num_seqs, uint16_t* q, int64_t q_stride,
+                    const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                    int64_t v_stride, const float* rope_cos, const float* rope_sin,
+                    int32_t max_pos, void* stream) {
+    if (num_seqs < 0) return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PKV_OK;
+    const int st = check_pool(pool);
+    if (st != PKV_OK) return st;
+    if (!block_table || !context_lens || !q || !k_new || !v_new || !rope_cos || !rope_sin)
+        return PKV_ERR_INVALID_ARG;
+    if (bt_stride < 1 || max_pos < 1) return PKV_ERR_INVALID_ARG;
+    if (q_stride < pkv::kQHeads * pkv::kHeadDim || k_stride < pkv::kKVHeads * pkv::kHeadDim ||
+        v_stride < pkv::kKVHeads * pkv::kHeadDim)
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope_cos) ||
+        !aligned16(rope_sin) || q_stride % 8 || k_stride % 8 || v_stride % 8)
+        return PKV_ERR_ALIGNMENT;
+    pkv::AppendParams p;
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.num_pages = pool->num_pages;
+    p.page_stride = pool->page_stride;
+    p.head_stride = pool->head_stride;
+    p.slot_stride = pool->slot_stride;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.q = q;
+    p.q_stride = q_stride;
+    p.k_new = k_new;
+    p.k_stride = k_stride;
+    p.v_new = v_new;
+    p.v_stride = v_stride;
+    p.rope_cos = rope_cos;
+    p.rope_sin = rope_sin;
+    p.max_pos = max_pos;
+    return hip_status(pkv::launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len) {
+    if (!pkv::plan_args_ok(num_seqs, max_context_len)) return 0;
+    return pkv::make_plan(num_seqs, max_context_len).splits;
+}
+
+size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_len) {
+    if (!pkv::plan_args_ok(num_seqs, max_context_len)) return 0;
+    return pkv::workspace_bytes(num_seqs, max_context_len);
+}
+
+int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
+                            int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, const uint16_t* q, int64_t q_stride,
+                            float scale, float* out, int64_t out_stride, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+                             max_context_len, q, q_stride, scale, out, out_stride, workspace,
+                             workspace_bytes);
+    if (c.status != PKV_OK || num_seqs == 0) return c.status;
+    return hip_status(pkv::launch_attn_split(c.params, static_cast<hipStream_t>(stream)));
+}
+
+int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, float* out, int64_t out_stride,
+                              const void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs < 0) return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PKV_OK;
+    if (!context_lens || !out || max_context_len < 1 || max_context_len > pkv::kMaxContext)
+        return PKV_ERR_INVALID_ARG;
+    if (out_stride < pkv::kQHeads * pkv::kHeadDim) return PKV_ERR_INVALID_ARG;
+    if (!aligned16(out) || out_stride % 4) return PKV_ERR_ALIGNMENT;
+    const pkv::Plan plan = pkv::make_plan(num_seqs, max_context_len);
+    if (plan.splits <= 1) return PKV_OK;
+    const size_t need = pkv::workspace_bytes(num_seqs, max_context_len);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGNMENT;
+    pkv::AttnParams p{};
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.max_context_len = max_context_len;
+    p.plan = plan;
+    p.out = out;
+    p.out_stride = out_stride;
+    const size_t acc_bytes =
+        (size_t)plan.splits * num_seqs * pkv::kQHeads * pkv::kHeadDim * sizeof(float);
+    p.ws_acc = static_cast<float*>(const_cast<void*>(workspace));
+    p.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(const_cast<void*>(workspace)) + acc_bytes);
+    return hip_status(pkv::launch_attn_combine(p, static_cast<hipStream_t>(stream)));
+}
+
+int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      const uint16_t* q, int64_t q_stride, float scale, float* out,
+                      int64_t out_stride, void* workspace, size_t workspace_bytes, void* stream) {
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+                             max_context_len, q, q_stride, scale, out, out_stride, workspace,
+                             workspace_bytes);
+    if (c.status != PKV_OK || num_seqs == 0) return c.status;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int st = hip_status(pkv::launch_attn_split(c.params, s));
+    if (st != PKV_OK || c.params.plan.splits <= 1) return st;
+    return hip_status(pkv::launch_attn_combine(c.params, s));
+}
+
+const char* paged_kv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_INVALID_ARG: return "invalid argument";
+        case PKV_ERR_ALIGNMENT: return "pointer or stride not 16-byte aligned";
+        case PKV_ERR_WORKSPACE: return "workspace smaller than paged_decode_attn_workspace_size()";
+        case PKV_ERR_UNSUPPORTED: return "unsupported geometry";
+        case PKV_ERR_HIP: return g_status_text[0] ? g_status_text : "HIP error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal interface between the C ABI layer (api.cpp) and the HIP kernels
+// (kernels.hip).  Not installed; the public ABI is include/paged_kv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kQHeads = 32;
+constexpr int kKVHeads = 8;
+constexpr int kGroup = kQHeads / kKVHeads;  // query heads per KV head
+constexpr int kHeadDim = 64;
+constexpr int kPageTokens = 16;
+constexpr int kMaxContext = 2048;
+constexpr int kPartialFloats = kHeadDim + 2;  // accumulator row + (max, sum)
+
+struct AppendParams {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int64_t num_pages, page_stride, head_stride, slot_stride;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    uint16_t* q;
+    int64_t q_stride;
+    const uint16_t* k_new;
+    int64_t k_stride;
+    const uint16_t* v_new;
+    int64_t v_stride;
+    const float* rope_cos;
+    const float* rope_sin;
+    int32_t max_pos;
+};
+
+// The split plan: S chunks of `pages_per_split` logical pages per sequence.
+struct Plan {
+    int32_t splits;
+    int32_t pages_per_split;
+};
+
+struct AttnParams {
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    int64_t num_pages, page_stride, head_stride, slot_stride;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* context_lens;
+    int32_t num_seqs;
+    int32_t max_context_len;
+    const uint16_t* q;
+    int64_t q_stride;
+    float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+    Plan plan;
+    float* out;
+    int64_t out_stride;
+    float* ws_acc;     // [num_seqs][32][S][64]
+    float2* ws_ml;     // [num_seqs][32][S] (running max in base-2 units, running sum)
+};
+
+Plan make_plan(int32_t num_seqs, int32_t max_context_len);
+size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len);
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);
+
+}  // namespace pkv
