@@ -72,40 +72,41 @@ def measured_traffic(splits: int):
 
 def cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s: float):
     """Time the FP64 oracle (append + attention) on whole (layer, sequence)
-    units of this workload: one unit on one thread to size the sample, then a
-    bounded sample spread over the host threads."""
+    units of this workload, reading a host copy of the pool: one unit on one
+    thread sizes the sample, then a bounded sample (about budget_s seconds of
+    CPU work, at most one full step) runs spread over the host threads."""
     import concurrent.futures
     import oracle
     from oracle import PoolView
-    from tests.gpu_util import gather_units
 
     orc = oracle.default()
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    rng = np.random.default_rng(1720)
+    pages = batch.pool_pages.cpu().numpy().view(np.uint16)
+    pool = PoolView.from_pages(pages)
+    bt_all = batch.block_tables.cpu().numpy()
+    ctx_all = batch.context_lens_host
     L, B = spec.num_layers, spec.num_seqs
-    all_units = [(int(rng.integers(L)), int(rng.integers(B))) for _ in range(4 * threads)]
+    units = [(layer, s) for layer in range(L) for s in range(B)]
+    np.random.default_rng(1720).shuffle(units)
 
-    def run_unit(u, data):
-        pages, bt, ctx, _ = data
+    def run_unit(u):
         layer, s = u
-        n = int(ctx[0])
+        bt = np.ascontiguousarray(bt_all[layer, s][None])
+        ctx = np.ascontiguousarray(ctx_all[s:s + 1])
         q = q0[layer, s][None].copy()
-        pv = PoolView.from_pages(pages)
-        orc.append(pv, bt, ctx, q, np.ascontiguousarray(k0[layer, s][None]),
+        orc.append(pool, bt, ctx, q, np.ascontiguousarray(k0[layer, s][None]),
                    np.ascontiguousarray(v0[layer, s][None]), rope[0], rope[1])
-        orc.attn(pv, bt, ctx, q, 0.125)
-        return n
+        orc.attn(pool, bt, ctx, q, 0.125)
+        return int(ctx[0])
 
-    data = {u: gather_units(batch, [u]) for u in all_units}
     t0 = time.perf_counter()
-    run_unit(all_units[0], data[all_units[0]])
+    run_unit(units[0])
     one = time.perf_counter() - t0
-    n_units = int(max(threads, min(len(all_units), budget_s * threads / max(one, 1e-3))))
-    n_units = max(threads, (n_units // threads) * threads)
-    sample = all_units[:n_units]
+    n_units = int(min(len(units), max(threads, budget_s / max(one, 1e-4))))
+    sample = units[:n_units]
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
-        ns = list(ex.map(lambda u: run_unit(u, data[u]), sample))
+        ns = list(ex.map(run_unit, sample))
     wall = time.perf_counter() - t0
     kv = sum(ns) * 2048
     return {
@@ -113,11 +114,12 @@ def cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s: float):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{len(sample)} (layer, sequence) units of this workload, each FP64 append "
-                   f"+ attention over its full context, spread over {threads} host threads"),
+        "sample": (f"{len(sample)} of the {len(units)} (layer, sequence) units of one step, "
+                   f"each FP64 append + attention over its full context, on {threads} host "
+                   f"threads (~{one * len(sample):.0f} s of CPU work)"),
         "seq_layers_per_s": round(len(sample) / wall, 3),
         "seconds": round(wall, 2),
-        "one_unit_one_thread_s": round(one, 3),
+        "one_unit_one_thread_s": round(one, 4),
     }
 
 
@@ -128,7 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 device copies of 256 MiB (reference for HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this decode-step library has no multi-GPU "
@@ -145,6 +149,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if a.copy_calibration:
+        src = torch.ones(128 * 2 ** 20, dtype=torch.int16, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": 256 * 2 ** 20, "copies": 8}))
+        return
     spec = wl.config_spec(a.config)
     log(f"[bench] config {a.config}: {spec.name}; building {spec.num_pages} pages on the GPU")
     pool = wl.make_device_pool(spec)
@@ -161,44 +173,45 @@ def main():
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step(events=None):
+    def step():
         for layer in range(L):
             batch.append(layer, stream)
-            if events is not None:
-                events[layer][0].record(stream)
             batch.attn_split(layer, stream)
-            if events is not None:
-                events[layer][1].record(stream)
             batch.attn_combine(layer, stream)
-            if events is not None:
-                events[layer][2].record(stream)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({a.warmup} steps); timing {a.steps} steps")
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)]
-           for _ in range(a.steps)]
+    # Pass A: the timed steps (no events inside: an event record costs a few us).
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for k in range(a.steps):
-        step(evs[k])
+    for _ in range(a.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / a.steps
-    split_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    comb_ms = [e[1].elapsed_time(e[2]) for st in evs for e in st]
-    split_avg = statistics.fmean(split_ms)
-    comb_avg = statistics.fmean(comb_ms)
-    attn_med = statistics.median([s + c for s, c in zip(split_ms, comb_ms)])
+    ms_per_step = start.elapsed_time(end) / a.steps
     assert torch.isfinite(batch.out).all(), "non-finite attention output"
+    # Pass B: the dominant kernel alone -- the split phase of every layer,
+    # K times, launched back to back on the same stream between two HIP
+    # events; its average launch duration matches the profiler's kernel time.
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(a.steps):
+        for layer in range(L):
+            batch.attn_split(layer, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    split_avg = start.elapsed_time(end) / (a.steps * L)
+    split_med = split_avg
 
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
     splits = batch.splits
+    if splits > 1:
+        log("[bench] note: this plan also launches the combine phase; attn_only covers the split phase")
     alg = split_bytes_per_launch(spec.ctx, splits)
     achieved = alg / (split_avg * 1e-3) / 1e9
     traffic = measured_traffic(splits)
@@ -225,13 +238,12 @@ def main():
         "frac_of_peak": round(kv_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "seq_layers_per_s": round(spec.num_seqs * L / (ms_per_step * 1e-3), 1),
         "attn_only": {
-            "kv_gbps": round(kv_layer / (attn_med * 1e-3) / 1e9, 2),
-            "frac_of_peak": round(kv_layer / (attn_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "us_per_layer_median": round(attn_med * 1e3, 2),
-            "seq_layers_per_s": round(spec.num_seqs / (attn_med * 1e-3), 1),
+            "kv_gbps": round(kv_layer / (split_med * 1e-3) / 1e9, 2),
+            "frac_of_peak": round(kv_layer / (split_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_per_layer": round(split_med * 1e3, 2),
+            "seq_layers_per_s": round(spec.num_seqs / (split_med * 1e-3), 1),
+            "combine_launched": splits > 1,
         },
-        "kernels_us_avg": {"attn_split": round(split_avg * 1e3, 2),
-                           "attn_combine": round(comb_avg * 1e3, 2)},
         "roofline": {
             "kernel": "attn_split_kernel",
             "bound": "hbm",

@@ -127,19 +127,22 @@ int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64
                     int32_t max_pos, void* stream);
 
 /*
- * Split plan of the decode attention.  The context of every sequence is cut
- * into chunks of whole pages; chunk c of a sequence covers logical pages
- * [c*P, (c+1)*P) where P = ceil(ceil(max_context_len/16) / S).  S depends only
- * on (num_seqs, max_context_len), so results are bitwise reproducible and
- * independent of where pages sit in the pool.  Returns S >= 1, or 0 for
- * arguments outside num_seqs >= 1, 1 <= max_context_len <= 2048.
+ * Split plan of the decode attention.  Each (sequence, KV head) is served by
+ * S workgroups of 4 wavefronts.  A sequence whose context fills np pages is
+ * cut into 4*S chunks of ceil(np / (4*S)) whole pages, in logical order; each
+ * wavefront streams one chunk, the 4 chunks of a workgroup are merged on
+ * chip, and when S > 1 the S workgroup partials are merged by the combine
+ * phase.  S depends only on (num_seqs, max_context_len) and the chunk
+ * boundaries only on each sequence's own length, so results are bitwise
+ * reproducible and independent of where pages sit in the pool.  Returns
+ * S >= 1, or 0 for arguments outside num_seqs >= 1, 1 <= max_context_len <= 2048.
  */
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
 
 /*
  * Bytes of device workspace paged_decode_attn needs for this plan: 0 when
- * S == 1, else S * num_seqs * 32 * 66 * 4 (per chunk and query head: 64
- * accumulator values, a running maximum and a running sum, FP32).
+ * S == 1, else S * num_seqs * 32 * 66 * 4 (per workgroup partial and query
+ * head: 64 accumulator values, a maximum and a sum, FP32).
  * Returns 0 for arguments outside the ranges above.
  */
 size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_len);
@@ -150,7 +153,7 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
  *   out[s][h*64 + d] = sum_{t<n} softmax_t(scale * q[s][h].K[t][h/4]) V[t][h/4][d]
  * over the logical token order t, where token t is read from page
  * block_table[s*bt_stride + t/16], slot t%16.  FP32 online softmax over BF16
- * inputs; the context is cut into S chunks (paged_decode_attn_num_splits)
+ * inputs; the context is cut into chunks (paged_decode_attn_num_splits)
  * whose partial results are merged with the log-sum-exp rule.  Rows with
  * n <= 0 are written as zeros.  Tokens at or past n, pages no table entry
  * below ceil(n/16) names, and table entries at or past ceil(n/16) are
@@ -178,10 +181,11 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
  * time or schedule them apart.  Enqueuing paged_decode_attn_split then
  * paged_decode_attn_combine on one stream with the same arguments is exactly
  * paged_decode_attn.  The split phase streams the pages and writes one
- * partial (maximum, sum, accumulator) per chunk into the workspace -- or,
+ * partial (maximum, sum, accumulator) per workgroup into the workspace -- or,
  * when S == 1, the final rows into out.  The combine phase merges the
- * partials into out; when S == 1 it enqueues nothing.  Same arguments,
- * checks and errors as paged_decode_attn.
+ * partials into out; when S == 1 it enqueues nothing.  The split phase takes
+ * the arguments, checks and errors of paged_decode_attn; the combine phase
+ * checks its own arguments the same way (INVALID_ARG, ALIGNMENT, WORKSPACE).
  */
 int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
                             int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,

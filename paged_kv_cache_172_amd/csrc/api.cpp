@@ -13,13 +13,14 @@
 
 namespace pkv {
 
-// Split planner.  A decode batch has num_seqs * 8 (sequence, KV head) units;
-// each chunk of a unit is one wavefront.  The plan aims for about
-// kTargetWaves wavefronts (a few per SIMD of a 256-CU part) so that small
-// batches still fill the chip, and never cuts chunks below kMinPagesPerSplit
-// pages.  It depends only on (num_seqs, max_context_len).
+// Split planner.  A decode batch has num_seqs * 8 (sequence, KV head)
+// units; each outer chunk of a unit is one workgroup of kChunkWaves
+// wavefronts.  The plan aims for about kTargetWaves wavefronts (two per SIMD
+// of a 256-CU part) so that small batches still fill the chip, and never cuts
+// chunks of a full-length context below kMinPagesPerSplit pages.  It depends
+// only on (num_seqs, max_context_len).
 #ifndef PKV_TARGET_WAVES
-#define PKV_TARGET_WAVES 3072
+#define PKV_TARGET_WAVES 2048
 #endif
 #ifndef PKV_MIN_PAGES_PER_SPLIT
 #define PKV_MIN_PAGES_PER_SPLIT 4
@@ -33,14 +34,12 @@ static bool plan_args_ok(int32_t num_seqs, int32_t max_context_len) {
 
 Plan make_plan(int32_t num_seqs, int32_t max_context_len) {
     const int32_t max_pages = (max_context_len + kPageTokens - 1) / kPageTokens;
-    const int64_t units = (int64_t)num_seqs * kKVHeads;
-    int64_t s = (kTargetWaves + units - 1) / units;
-    const int32_t s_cap = (max_pages + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+    const int64_t waves_per_split = (int64_t)num_seqs * kKVHeads * kChunkWaves;
+    int64_t s = (kTargetWaves + waves_per_split - 1) / waves_per_split;
+    const int64_t s_cap = max_pages / ((int64_t)kChunkWaves * kMinPagesPerSplit);
     if (s > s_cap) s = s_cap;
     if (s < 1) s = 1;
-    const int32_t pps = (int32_t)((max_pages + s - 1) / s);
-    const int32_t splits = (max_pages + pps - 1) / pps;
-    return Plan{splits, pps};
+    return Plan{(int32_t)s};
 }
 
 size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len) {

@@ -35,10 +35,12 @@ struct AppendParams {
     int32_t max_pos;
 };
 
-// The split plan: S chunks of `pages_per_split` logical pages per sequence.
+// The split plan: S outer chunks per (sequence, KV head), each one workgroup
+// of kChunkWaves waves; a sequence of np pages is cut into kChunkWaves * S
+// chunks of ceil(np / (kChunkWaves * S)) pages.
+constexpr int kChunkWaves = 4;
 struct Plan {
     int32_t splits;
-    int32_t pages_per_split;
 };
 
 struct AttnParams {
@@ -57,7 +59,7 @@ struct AttnParams {
     float* out;
     int64_t out_stride;
     float* ws_acc;     // [num_seqs][32][S][64]
-    float2* ws_ml;     // [num_seqs][32][S] (running max in base-2 units, running sum)
+    float2* ws_ml;     // [num_seqs][32][S] (maximum in base-2 units, sum)
 };
 
 Plan make_plan(int32_t num_seqs, int32_t max_context_len);

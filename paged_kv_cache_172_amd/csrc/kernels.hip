@@ -83,16 +83,11 @@ __device__ __forceinline__ T uniform(T x) {
     return __builtin_amdgcn_readfirstlane(x);
 }
 
-__device__ __forceinline__ uint4 load16(const char* base, uint32_t byte_off) {
-    return *reinterpret_cast<const uint4*>(base + byte_off);
-}
-
 // ------------------------------------------------------------- append --
 
 // Round an FP64 value to the nearest BF16 bit pattern, ties to even, in one
 // step from the FP64 bits (no intermediate FP32 rounding).
-__device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
-    const uint64_t u = __double_as_longlong(y);
+__device__ __noinline__ uint32_t f64_to_bf16_rne_slow(uint64_t u) {
     const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
     const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
     if (mag > 0x7FF0000000000000ull) return sign | 0x7FC0u;  // NaN
@@ -121,96 +116,126 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
     return sign | ((uint32_t)eb << 7) | ((uint32_t)kept & 0x7Fu);
 }
 
-// Rotate 8 pairs (i0+e, i0+e+32), e < 8, of one head vector at table row pos,
-// in FP64, and round each result once to BF16.  x1 holds dims i0..i0+7 and x2
-// dims i0+32..i0+39 as packed BF16 pairs.
-__device__ __forceinline__ void rope8(uint4& x1, uint4& x2, const float* crow, const float* srow) {
-    const float4 c0 = *reinterpret_cast<const float4*>(crow);
-    const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
-    const float4 s0 = *reinterpret_cast<const float4*>(srow);
-    const float4 s1 = *reinterpret_cast<const float4*>(srow + 4);
-    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    uint32_t a[4] = {x1.x, x1.y, x1.z, x1.w};
-    uint32_t b[4] = {x2.x, x2.y, x2.z, x2.w};
-    uint32_t ya[4], yb[4];
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
+    const uint64_t u = __double_as_longlong(y);
+    const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+    // |y| in [2^-126, (2 - 2^-8) * 2^127): the result is a normal BF16.  Add the
+    // round-half-even bias below the 7 kept mantissa bits and rebias the
+    // exponent from 1023 to 127 (a carry into the exponent is the binade step).
+    if (mag >= 0x3810000000000000ull && mag < 0x47EFF00000000000ull) {
+        const uint64_t t = mag + 0x00000FFFFFFFFFFFull + ((mag >> 45) & 1ull);
+        return ((uint32_t)(u >> 48) & 0x8000u) | (uint32_t)((t >> 45) - (896ull << 7));
+    }
+    return f64_to_bf16_rne_slow(u);
+}
+
+// Rotate the 4 pairs (i0+e, i0+e+32), e < 4, of one head vector with the
+// table row of the new token's position, in FP64, and round each result once
+// to BF16.  x1 holds dims i0..i0+3 and x2 dims i0+32..i0+35 as BF16 pairs.
+__device__ __forceinline__ void rope4(uint2& x1, uint2& x2, float4 c, float4 sn) {
+    const uint32_t a[2] = {x1.x, x1.y};
+    const uint32_t b[2] = {x2.x, x2.y};
+    const float cs[4] = {c.x, c.y, c.z, c.w};
+    const float ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    uint32_t ya[2], yb[2];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < 2; ++w) {
         uint32_t lo_a = 0, lo_b = 0;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int e = 2 * w + half;
             const double u1 = (double)(half ? bf16_hi(a[w]) : bf16_lo(a[w]));
             const double u2 = (double)(half ? bf16_hi(b[w]) : bf16_lo(b[w]));
-            const double c = (double)cs[e];
-            const double s = (double)sn[e];
+            const double cc = (double)cs[e];
+            const double s = (double)ss[e];
             // Both products are exact in FP64 (8 x 24 significant bits), so
             // each line rounds once, whatever the compiler contracts.
-            const uint32_t r1 = f64_to_bf16_rne(u1 * c - u2 * s);
-            const uint32_t r2 = f64_to_bf16_rne(u2 * c + u1 * s);
-            lo_a |= r1 << (16 * half);
-            lo_b |= r2 << (16 * half);
+            lo_a |= f64_to_bf16_rne(u1 * cc - u2 * s) << (16 * half);
+            lo_b |= f64_to_bf16_rne(u2 * cc + u1 * s) << (16 * half);
         }
         ya[w] = lo_a;
         yb[w] = lo_b;
     }
-    x1 = make_uint4(ya[0], ya[1], ya[2], ya[3]);
-    x2 = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+    x1 = make_uint2(ya[0], ya[1]);
+    x2 = make_uint2(yb[0], yb[1]);
 }
 
-// One block per sequence, 256 threads:
-//   threads   0..127  rotate q: head tid/4, pairs (tid%4)*8 .. +7
-//   threads 128..159  rotate k: head (tid-128)/4, written to the page slot
-//   threads 160..223  copy v: 16 bytes each, written to the page slot
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-    const int s = blockIdx.x;
+// Three 128-thread blocks per sequence; a task is 4 rotation pairs of one head
+// (or 16 bytes of V):
+//   blocks 0, 1: q tasks 0..255 (head task/8, pairs (task%8)*4 .. +3)
+//   block 2:     threads 0..63 k tasks (head t/8), threads 64..127 copy V.
+// The new-token rows are loaded before the length is known (they do not
+// depend on it); the table row and the page index follow from the length.
+constexpr int kAppendThreads = 128;
+constexpr int kAppendBlocksPerSeq = 3;
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
+    const int s = blockIdx.x / kAppendBlocksPerSeq;
+    const int part = blockIdx.x % kAppendBlocksPerSeq;
     const int tid = threadIdx.x;
+    const bool is_v = part == 2 && tid >= 64;
+    // head-vector base and pair offset of this thread's task
+    int head, i0;
+    const uint16_t* src;
+    if (part < 2) {
+        const int task = part * kAppendThreads + tid;
+        head = task >> 3;
+        i0 = (task & 7) * 4;
+        src = p.q + (int64_t)s * p.q_stride + head * kHeadDim;
+    } else if (!is_v) {
+        head = tid >> 3;
+        i0 = (tid & 7) * 4;
+        src = p.k_new + (int64_t)s * p.k_stride + head * kHeadDim;
+    } else {
+        head = (tid - 64) >> 3;
+        i0 = ((tid - 64) & 7) * 8;
+        src = p.v_new + (int64_t)s * p.v_stride + head * kHeadDim;
+    }
+    uint2 x1 = make_uint2(0, 0), x2 = make_uint2(0, 0);
+    uint4 vrow = make_uint4(0, 0, 0, 0);
+    if (is_v) {
+        vrow = *reinterpret_cast<const uint4*>(src + i0);
+    } else {
+        x1 = *reinterpret_cast<const uint2*>(src + i0);
+        x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
+    }
     const int n = p.context_lens[s];
     if (n < 1) return;
     const int pos = n - 1;
     if (pos >= p.max_pos) return;                 // outside the RoPE table: not dereferenced
-    const int64_t j = pos >> 4;
+    int64_t page = -1;
     const int slot = pos & 15;
-    if (j >= p.bt_stride) return;
-    const int64_t page = p.block_table[(int64_t)s * p.bt_stride + j];
-    const bool page_ok = page >= 0 && page < p.num_pages;
-    const float* crow = p.rope_cos + (int64_t)pos * 32;
-    const float* srow = p.rope_sin + (int64_t)pos * 32;
-    if (tid < 128) {
-        const int h = tid >> 2, i0 = (tid & 3) * 8;
-        uint16_t* base = p.q + (int64_t)s * p.q_stride + h * kHeadDim;
-        uint4 x1 = *reinterpret_cast<const uint4*>(base + i0);
-        uint4 x2 = *reinterpret_cast<const uint4*>(base + i0 + 32);
-        rope8(x1, x2, crow + i0, srow + i0);
-        *reinterpret_cast<uint4*>(base + i0) = x1;
-        *reinterpret_cast<uint4*>(base + i0 + 32) = x2;
-    } else if (tid < 160) {
-        if (!page_ok) return;
-        const int g = (tid - 128) >> 2, i0 = ((tid - 128) & 3) * 8;
-        const uint16_t* src = p.k_new + (int64_t)s * p.k_stride + g * kHeadDim;
-        uint4 x1 = *reinterpret_cast<const uint4*>(src + i0);
-        uint4 x2 = *reinterpret_cast<const uint4*>(src + i0 + 32);
-        rope8(x1, x2, crow + i0, srow + i0);
-        uint16_t* dst = p.k_pool + page * p.page_stride + g * p.head_stride + slot * p.slot_stride;
-        *reinterpret_cast<uint4*>(dst + i0) = x1;
-        *reinterpret_cast<uint4*>(dst + i0 + 32) = x2;
-    } else if (tid < 224) {
-        if (!page_ok) return;
-        const int chunk = tid - 160, g = chunk >> 3, d0 = (chunk & 7) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(p.v_new + (int64_t)s * p.v_stride +
-                                                        g * kHeadDim + d0);
-        uint16_t* dst = p.v_pool + page * p.page_stride + g * p.head_stride + slot * p.slot_stride;
-        *reinterpret_cast<uint4*>(dst + d0) = v;
+    if (part == 2) {
+        const int64_t j = pos >> 4;
+        if (j >= p.bt_stride) return;
+        page = p.block_table[(int64_t)s * p.bt_stride + j];
+        if (page < 0 || page >= p.num_pages) return;   // never write through a bad entry
     }
+    if (is_v) {
+        uint16_t* dst = p.v_pool + page * p.page_stride + head * p.head_stride + slot * p.slot_stride;
+        *reinterpret_cast<uint4*>(dst + i0) = vrow;
+        return;
+    }
+    const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * 32 + i0);
+    const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * 32 + i0);
+    rope4(x1, x2, c, sn);
+    uint16_t* dst = part < 2
+        ? const_cast<uint16_t*>(src)
+        : p.k_pool + page * p.page_stride + head * p.head_stride + slot * p.slot_stride;
+    *reinterpret_cast<uint2*>(dst + i0) = x1;
+    *reinterpret_cast<uint2*>(dst + i0 + 32) = x2;
 }
 
 // ---------------------------------------------------------- attention --
 //
-// One wavefront per work unit (sequence s, KV head g, chunk c); it serves the
-// 4 query heads 4g..4g+3.  Inside a page the 64 lanes are 16 quads: quad t
-// (lanes 4t..4t+3) owns token slot t, and lane quarter c4 = lane%4 owns dims
-// [8*c4, 8*c4+8) and [32+8*c4, 32+8*c4+8) of that token's K and V row (two
-// 16-byte loads each; four consecutive lanes read 64 contiguous bytes).
+// One workgroup of 4 wavefronts per (sequence s, KV head g, outer chunk ci);
+// it serves the 4 query heads 4g..4g+3.  The sequence's np pages are cut into
+// 4*S chunks of ceil(np / (4*S)) pages and wave w takes chunk 4*ci + w, so the
+// chunk boundaries follow each sequence's own length.  Inside a page the 64
+// lanes are 16 quads: quad t (lanes 4t..4t+3) owns token slot t, and lane
+// quarter c4 = lane%4 owns dims [8*c4, 8*c4+8) and [32+8*c4, 32+8*c4+8) of that
+// token's K and V row (two 16-byte loads each; four consecutive lanes read 64
+// contiguous bytes).
 //
 // Per page: QK^T is 8 v_dot2_f32_bf16 per head per lane plus a 2-step DPP
 // quad sum; every quad then runs its own FP32 online softmax over the tokens
@@ -218,12 +243,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // raised only when a logit exceeds it by more than kRescaleSlack (base-2
 // units; values p = 2^(x - m) stay below 2^kRescaleSlack, so nothing
 // overflows).  At the end of the chunk the 16 quads are merged with the
-// log-sum-exp rule through permlane swaps and DPP, and the wave writes one
-// partial (max, sum, 64-wide accumulator) per query head, or the normalised
-// output when the plan has a single chunk.
+// log-sum-exp rule through permlane swaps and DPP, the 4 waves of the
+// workgroup are merged the same way through LDS, and the workgroup writes the
+// normalised output (S = 1) or one partial (max, sum, 64-wide accumulator) per
+// query head for the combine kernel (S > 1).
 
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kWavesPerBlock = 4;
+#ifndef PKV_RING
+#define PKV_RING 3
+#endif
+constexpr int kRing = PKV_RING;  // page buffers per wave: kRing-1 pages in flight
+static_assert(kRing >= 2 && kRing <= 8, "ring size");
 #ifndef PKV_SPLIT_WAVES_PER_EU
 #define PKV_SPLIT_WAVES_PER_EU 3
 #endif
@@ -238,15 +268,52 @@ struct SoftmaxState {
     float acc[kGroup][16];
 };
 
-__device__ __forceinline__ PageRegs load_page(const char* kbase, const char* vbase,
+// Buffer descriptor for one (page, KV head) tile: 48-bit base, raw
+// (stride 0), `bytes` of range.  A descriptor with 0 bytes turns the load
+// into a no-op that returns zeros without touching memory, which is how
+// prefetches past the end of a chunk are issued without branches.
+constexpr int32_t kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferWord3);
+}
+
+#ifndef PKV_LOAD_POLICY
+#define PKV_LOAD_POLICY 0
+#endif
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, PKV_LOAD_POLICY);
+    return __builtin_bit_cast(uint4, v);
+}
+
+__device__ __forceinline__ PageRegs load_page(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                               uint32_t off_a, uint32_t off_b) {
     PageRegs r;
-    r.ka = load16(kbase, off_a);
-    r.kb = load16(kbase, off_b);
-    r.va = load16(vbase, off_a);
-    r.vb = load16(vbase, off_b);
+    r.ka = buffer_load16(kr, off_a);
+    r.kb = buffer_load16(kr, off_b);
+    r.va = buffer_load16(vr, off_a);
+    r.vb = buffer_load16(vr, off_b);
     return r;
 }
+
+// Up to 8 page buffers addressed only by compile-time indices, so they live
+// in VGPRs (an array indexed in a loop with an early exit can end up in
+// scratch memory).
+struct PageRing {
+    PageRegs s0, s1, s2, s3, s4, s5, s6, s7;
+    template <int I>
+    __device__ __forceinline__ PageRegs& at() {
+        static_assert(I >= 0 && I < 8, "ring slot");
+        if constexpr (I == 0) return s0;
+        else if constexpr (I == 1) return s1;
+        else if constexpr (I == 2) return s2;
+        else if constexpr (I == 3) return s3;
+        else if constexpr (I == 4) return s4;
+        else if constexpr (I == 5) return s5;
+        else if constexpr (I == 6) return s6;
+        else return s7;
+    }
+};
 
 template <bool kMasked>
 __device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGroup],
@@ -280,7 +347,7 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGro
     float excess = x[0] - st.m[0];
 #pragma unroll
     for (int r = 1; r < kGroup; ++r) excess = fmaxf(excess, x[r] - st.m[r]);
-    if (__builtin_amdgcn_ballot_w64(excess > kRescaleSlack)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(excess > kRescaleSlack) != 0, 0)) {
 #pragma unroll
         for (int r = 0; r < kGroup; ++r) {
             // Only heads whose logit jumped rescale; the others keep alpha = 1
@@ -310,42 +377,68 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGro
     }
 }
 
-__global__ __launch_bounds__(kWavesPerBlock * 64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
+// A round is kRing straight-line steps (unrolled by template recursion, so
+// every ring slot index is a compile-time constant).  Invariant at the start
+// of a round: slots 0..kRing-2 hold pages j..j+kRing-2 (issued), slot
+// kRing-1 is free.  Step I issues page j+kRing-1 into the slot freed by the
+// previous step, then consumes slot I.
+template <int I, typename Issue>
+__device__ __forceinline__ void ring_round(PageRing& ring, int& j, const uint4 (&qa)[kGroup],
+                                           const uint4 (&qb)[kGroup], float sl2,
+                                           SoftmaxState& st, Issue& issue) {
+    if constexpr (I < kRing) {
+        ring.template at<(I + kRing - 1) % kRing>() = issue(j + kRing - 1);
+        consume_page<false>(ring.template at<I>(), qa, qb, sl2, true, st);
+        ++j;
+        ring_round<I + 1>(ring, j, qa, qb, sl2, st, issue);
+    }
+}
+
+// The last 1..kRing pages of a chunk sit in slots 0..left-1; they are
+// consumed with the slot mask (only the chunk's last page can be partial).
+template <int I>
+__device__ __forceinline__ void ring_tail(PageRing& ring, int j, int left, int n, int t,
+                                          const uint4 (&qa)[kGroup], const uint4 (&qb)[kGroup],
+                                          float sl2, SoftmaxState& st) {
+    if constexpr (I < kRing) {
+        if (I < left) {
+            consume_page<true>(ring.template at<I>(), qa, qb, sl2, t < n - (j + I) * kPageTokens, st);
+            ring_tail<I + 1>(ring, j, left, n, t, qa, qb, sl2, st);
+        }
+    }
+}
+
+template <int I, typename Issue>
+__device__ __forceinline__ void ring_fill(PageRing& ring, int pb, Issue& issue) {
+    if constexpr (I < kRing - 1) {
+        ring.template at<I>() = issue(pb + I);
+        ring_fill<I + 1>(ring, pb, issue);
+    }
+}
+
+__global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
 void attn_split_kernel(AttnParams p) {
+    // Partials of the workgroup's 4 waves: [wave][head][64 dims] and (max, sum).
+    __shared__ float lds_acc[kChunkWaves][kGroup][kHeadDim];
+    __shared__ float2 lds_ml[kChunkWaves][kGroup];
+
     const int lane = threadIdx.x & 63;
-    const int wave = uniform((int)(threadIdx.x >> 6));
-    const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave;  // g fastest, then s, then c
-    const int g = (int)(unit % kKVHeads);
-    const int64_t sc = unit / kKVHeads;
-    const int s = (int)(sc % p.num_seqs);
-    const int c = (int)(sc / p.num_seqs);
-    if (c >= p.plan.splits) return;
-
-    int n = uniform(p.context_lens[s]);
-    n = n < p.max_context_len ? n : p.max_context_len;
-    const int np = n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
-    const int pb = c * p.plan.pages_per_split;
-    const int pe = min(pb + p.plan.pages_per_split, np);
-
+    const int w = uniform((int)(threadIdx.x >> 6));
+    const uint32_t wg = blockIdx.x;                    // g fastest, then s, then outer chunk
+    const int g = (int)(wg % kKVHeads);
+    const uint32_t rest = wg / kKVHeads;
+    const int s = (int)(rest % (uint32_t)p.num_seqs);
+    const int ci = (int)(rest / (uint32_t)p.num_seqs);
     const int t = lane >> 2;   // token slot owned by this lane's quad
     const int c4 = lane & 3;   // dim quarter owned inside the quad
-    const bool single = p.plan.splits == 1;
 
-    if (pb >= pe) {            // empty chunk: only a zero-length context needs a write
-        if (single) {
-            float* orow = p.out + (int64_t)s * p.out_stride + (kGroup * g) * kHeadDim;
-            *reinterpret_cast<float4*>(orow + lane * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        return;
-    }
-
-    // This chunk's table entries, one per lane (at most 128 pages per chunk).
-    const int32_t* bt_row = p.block_table + (int64_t)s * p.bt_stride + pb;
-    const int cnt = pe - pb;
-    const int32_t tbl0 = lane < cnt ? bt_row[lane] : 0;
-    const int32_t tbl1 = lane + 64 < cnt ? bt_row[lane + 64] : 0;
-
-    // q of the 4 query heads, this lane's 16 dims, as packed BF16 pairs.
+    // Independent loads first: the table row (first 128 entries, one per
+    // lane in two registers), q of the 4 query heads, and the length.
+    const int32_t* bt_row = p.block_table + (int64_t)s * p.bt_stride;
+    const int bt_w = p.bt_stride < kMaxContext / kPageTokens ? (int)p.bt_stride
+                                                              : kMaxContext / kPageTokens;
+    const int32_t tbl0 = lane < bt_w ? bt_row[lane] : 0;
+    const int32_t tbl1 = lane + 64 < bt_w ? bt_row[lane + 64] : 0;
     uint4 qa[kGroup], qb[kGroup];
     const uint16_t* qrow = p.q + (int64_t)s * p.q_stride + (kGroup * g) * kHeadDim;
 #pragma unroll
@@ -353,177 +446,194 @@ void attn_split_kernel(AttnParams p) {
         qa[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + c4 * 8);
         qb[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + 32 + c4 * 8);
     }
+    int n = uniform(p.context_lens[s]);
+    n = n < p.max_context_len ? n : p.max_context_len;
+    const int np = n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
 
-    const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
-    const uint32_t off_b = off_a + 64;
-    const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
-    const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
-    const int64_t page_bytes = p.page_stride * 2;
+    // This wave's chunk: the sequence's np pages are cut into 4*S chunks of
+    // ceil(np / (4*S)) pages; wave w of outer chunk ci takes chunk 4*ci + w.
+    const int nchunks = kChunkWaves * p.plan.splits;
+    const int cs = (np + nchunks - 1) / nchunks;
+    const int pb = (kChunkWaves * ci + w) * cs;
+    const int pe = min(pb + cs, np);
+
+    float u[16];          // after the wave merge: row R's head, this lane's 16 dims
+    float mrow = -INFINITY, lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) u[k] = 0.0f;
     bool bad_page = false;
 
-    auto page_base = [&](int j, const char*& kb, const char*& vb) {
-        const int idx = j - pb;
-        int32_t phys = idx < 64 ? __builtin_amdgcn_readlane(tbl0, idx)
-                                : __builtin_amdgcn_readlane(tbl1, idx - 64);
-        if (phys < 0 || phys >= p.num_pages) {  // never dereference a bad entry
-            bad_page = true;
-            phys = 0;
+    if (pb < pe) {
+        const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
+        const uint32_t off_b = off_a + 64;
+        const int32_t tile_bytes = (int32_t)((15 * p.slot_stride + kHeadDim) * 2);
+        const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
+        const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
+        const int64_t page_bytes = p.page_stride * 2;
+
+        SoftmaxState st;
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) {
+            st.m[r] = -INFINITY;
+            st.l[r] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) st.acc[r][k] = 0.0f;
         }
-        kb = kpool + (int64_t)phys * page_bytes;
-        vb = vpool + (int64_t)phys * page_bytes;
-    };
+        const float sl2 = p.scale_log2;
 
-    SoftmaxState st;
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-        st.m[r] = -INFINITY;
-        st.l[r] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) st.acc[r][k] = 0.0f;
-    }
-    const float sl2 = p.scale_log2;
+        // Issue the loads of logical page j (a no-op load when j >= pe).
+        auto issue = [&](int j) {
+            const bool live = j < pe;
+            const int idx = j < pe - 1 ? j : pe - 1;
+            int32_t phys = idx < 64 ? __builtin_amdgcn_readlane(tbl0, idx)
+                                    : __builtin_amdgcn_readlane(tbl1, idx - 64);
+            if (phys < 0 || phys >= p.num_pages) {  // never dereference a bad entry
+                bad_page |= live;
+                phys = 0;
+            }
+            const int32_t bytes = live ? tile_bytes : 0;
+            const int64_t off = (int64_t)phys * page_bytes;
+            return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), off_a,
+                             off_b);
+        };
 
-    // Pages pb .. pe-1 with two pages in flight ahead of the one consumed.
-    const char *kb, *vb;
-    page_base(pb, kb, vb);
-    PageRegs cur = load_page(kb, vb, off_a, off_b);
-    PageRegs nxt = cur;
-    if (pb + 1 < pe) {
-        page_base(pb + 1, kb, vb);
-        nxt = load_page(kb, vb, off_a, off_b);
-    }
-    int j = pb;
-    for (; j + 2 < pe; ++j) {
-        page_base(j + 2, kb, vb);
-        PageRegs nn = load_page(kb, vb, off_a, off_b);
-        consume_page<false>(cur, qa, qb, sl2, true, st);
-        cur = nxt;
-        nxt = nn;
-    }
-    if (j + 1 < pe) {
-        consume_page<false>(cur, qa, qb, sl2, true, st);
-        cur = nxt;
-        ++j;
-    }
-    // Last page of the chunk: the only one that can hold slots past n.
-    const int valid_tokens = n - j * kPageTokens;
-    consume_page<true>(cur, qa, qb, sl2, t < valid_tokens, st);
+        // Ring of kRing page buffers: while page j is consumed, pages j+1 ..
+        // j+kRing-1 are in flight.  The last page of the chunk is the only
+        // one that can hold slots past n, so it is consumed with the mask.
+        PageRing ring;
+        ring_fill<0>(ring, pb, issue);
+        int j = pb;
+        const int rounds = (pe - 1 - pb) / kRing;   // whole rounds of unmasked pages
+        for (int r = 0; r < rounds; ++r) ring_round<0>(ring, j, qa, qb, sl2, st, issue);
+        ring.template at<kRing - 1>() = issue(j + kRing - 1);
+        ring_tail<0>(ring, j, pe - j, n, t, qa, qb, sl2, st);
 
-    // ---- merge the 16 quads of the wave (log-sum-exp rule) ----
-    float M[kGroup];
+        // ---- merge the 16 quads of the wave (log-sum-exp rule) ----
+        float M[kGroup];
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) M[r] = max_over_quads(st.m[r]);  // finite: slot 0 is valid
+        for (int r = 0; r < kGroup; ++r) M[r] = max_over_quads(st.m[r]);  // finite: slot pb*16 is valid
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-        const float alpha = st.m[r] == -INFINITY ? 0.0f : exp2_fast(st.m[r] - M[r]);
-        st.l[r] *= alpha;
+        for (int r = 0; r < kGroup; ++r) {
+            const float alpha = st.m[r] == -INFINITY ? 0.0f : exp2_fast(st.m[r] - M[r]);
+            st.l[r] *= alpha;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) st.acc[r][k] *= alpha;
+            for (int k = 0; k < 16; ++k) st.acc[r][k] *= alpha;
+        }
+        // Sum over lane bit 5 (permlane32 swap): lanes 0..31 keep heads 0/1,
+        // 32..63 heads 2/3; then over lane bit 4 (permlane16 swap): row R
+        // (lanes 16R..16R+15) keeps head R.
+        {
+            float t0[16], t1[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                Pair a = swap32(st.acc[0][k], st.acc[2][k]);
+                t0[k] = a.a + a.b;
+                Pair b = swap32(st.acc[1][k], st.acc[3][k]);
+                t1[k] = b.a + b.b;
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                Pair a = swap16(t0[k], t1[k]);
+                u[k] = a.a + a.b;
+            }
+            Pair la = swap32(st.l[0], st.l[2]);
+            Pair lb = swap32(st.l[1], st.l[3]);
+            Pair lc = swap16(la.a + la.b, lb.a + lb.b);
+            lsum = lc.a + lc.b;
+        }
+        // Sum over lane bits 2..3 (the 4 quads of a row) with DPP row rotations.
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            u[k] += dpp<kDppRowRor4>(u[k]);
+            u[k] += dpp<kDppRowRor8>(u[k]);
+        }
+        lsum += dpp<kDppRowRor4>(lsum);
+        lsum += dpp<kDppRowRor8>(lsum);
+        const int row = lane >> 4;
+        mrow = M[0];
+        mrow = row == 1 ? M[1] : mrow;
+        mrow = row == 2 ? M[2] : mrow;
+        mrow = row == 3 ? M[3] : mrow;
+        if (bad_page) lsum = NAN;
     }
-    // Sum over lane bit 5 (permlane32 swap): lanes 0..31 keep heads 0/1, 32..63 heads 2/3;
-    // then over lane bit 4 (permlane16 swap): row R (lanes 16R..16R+15) keeps head R.
-    float u[16];
-    float lsum;
+
+    // ---- merge the 4 chunks of the workgroup through LDS ----
     {
-        float t0[16], t1[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            Pair a = swap32(st.acc[0][k], st.acc[2][k]);
-            t0[k] = a.a + a.b;
-            Pair b = swap32(st.acc[1][k], st.acc[3][k]);
-            t1[k] = b.a + b.b;
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            Pair a = swap16(t0[k], t1[k]);
-            u[k] = a.a + a.b;
-        }
-        Pair la = swap32(st.l[0], st.l[2]);
-        Pair lb = swap32(st.l[1], st.l[3]);
-        Pair lc = swap16(la.a + la.b, lb.a + lb.b);
-        lsum = lc.a + lc.b;
+        const int row = lane >> 4;               // query head 4g + row
+        const int qd = (lane >> 2) & 3;          // which 4 of the lane's 16 values it stores
+        float4 v4;
+        v4.x = qd == 0 ? u[0] : qd == 1 ? u[4] : qd == 2 ? u[8] : u[12];
+        v4.y = qd == 0 ? u[1] : qd == 1 ? u[5] : qd == 2 ? u[9] : u[13];
+        v4.z = qd == 0 ? u[2] : qd == 1 ? u[6] : qd == 2 ? u[10] : u[14];
+        v4.w = qd == 0 ? u[3] : qd == 1 ? u[7] : qd == 2 ? u[11] : u[15];
+        const int dim0 = c4 * 8 + (qd & 1) * 4 + (qd >> 1) * 32;
+        *reinterpret_cast<float4*>(&lds_acc[w][row][dim0]) = v4;
+        if ((lane & 15) == 0) lds_ml[w][row] = make_float2(mrow, lsum);
     }
-    // Sum over lane bits 2..3 (the 4 quads of a row) with DPP row rotations.
+    __syncthreads();
+    // Wave w finishes query head 4g + w; lane = output dim.
+    const int r = w;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        u[k] += dpp<kDppRowRor4>(u[k]);
-        u[k] += dpp<kDppRowRor8>(u[k]);
+    for (int i = 0; i < kChunkWaves; ++i) Mx = fmaxf(Mx, lds_ml[i][r].x);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kChunkWaves; ++i) {
+        const float2 ml = lds_ml[i][r];
+        const float wt = ml.x == -INFINITY ? 0.0f : exp2_fast(ml.x - Mx);
+        L = fmaf(wt, ml.y, L);
+        o = fmaf(wt, lds_acc[i][r][lane], o);
     }
-    lsum += dpp<kDppRowRor4>(lsum);
-    lsum += dpp<kDppRowRor8>(lsum);
-
-    const int row = lane >> 4;              // query head 4g + row
-    const int qd = (lane >> 2) & 3;         // which 4 of the lane's 16 values it stores
-    float mrow = M[0];
-    mrow = row == 1 ? M[1] : mrow;
-    mrow = row == 2 ? M[2] : mrow;
-    mrow = row == 3 ? M[3] : mrow;
-    float4 v4;
-    v4.x = qd == 0 ? u[0] : qd == 1 ? u[4] : qd == 2 ? u[8] : u[12];
-    v4.y = qd == 0 ? u[1] : qd == 1 ? u[5] : qd == 2 ? u[9] : u[13];
-    v4.z = qd == 0 ? u[2] : qd == 1 ? u[6] : qd == 2 ? u[10] : u[14];
-    v4.w = qd == 0 ? u[3] : qd == 1 ? u[7] : qd == 2 ? u[11] : u[15];
-    const int dim0 = c4 * 8 + (qd & 1) * 4 + (qd >> 1) * 32;
-    const int h = kGroup * g + row;
-    if (bad_page) lsum = NAN;
-    if (single) {
-        const float inv = 1.0f / lsum;
-        float* orow = p.out + (int64_t)s * p.out_stride + h * kHeadDim;
-        *reinterpret_cast<float4*>(orow + dim0) =
-            make_float4(v4.x * inv, v4.y * inv, v4.z * inv, v4.w * inv);
+    const int h = kGroup * g + r;
+    if (p.plan.splits == 1) {
+        p.out[(int64_t)s * p.out_stride + h * kHeadDim + lane] = L == 0.0f ? 0.0f : o / L;
     } else {
-        const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + c;
-        *reinterpret_cast<float4*>(p.ws_acc + slot_idx * kHeadDim + dim0) = v4;
-        if ((lane & 15) == 0) p.ws_ml[slot_idx] = make_float2(mrow, lsum);
+        const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + ci;
+        p.ws_acc[slot_idx * kHeadDim + lane] = o;
+        if (lane == 0) p.ws_ml[slot_idx] = make_float2(Mx, L);
     }
 }
 
-// One thread per (sequence, query head, 4 output dims).
+// One thread per (sequence, query head, 4 output dims): merges the S
+// outer-chunk partials with the log-sum-exp rule (empty ones weigh 0).
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int d4 = (int)(tid & 15);
     const int h = (int)((tid >> 4) & 31);
     const int64_t s = tid >> 9;
     if (s >= p.num_seqs) return;
-    int n = p.context_lens[s];
-    n = n < p.max_context_len ? n : p.max_context_len;
-    const int np = n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
     const int S = p.plan.splits;
-    const int nc = (np + p.plan.pages_per_split - 1) / p.plan.pages_per_split;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (nc > 0) {
-        const int64_t base = ((int64_t)s * kQHeads + h) * S;
-        float M = -INFINITY;
-        for (int c = 0; c < nc; ++c) M = fmaxf(M, p.ws_ml[base + c].x);
-        float L = 0.0f;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int c = 0; c < nc; ++c) {
-            const float2 ml = p.ws_ml[base + c];
-            const float w = ml.x == -INFINITY ? 0.0f : exp2_fast(ml.x - M);
-            const float4 v = *reinterpret_cast<const float4*>(p.ws_acc + (base + c) * kHeadDim + d4 * 4);
-            L = fmaf(w, ml.y, L);
-            a.x = fmaf(w, v.x, a.x);
-            a.y = fmaf(w, v.y, a.y);
-            a.z = fmaf(w, v.z, a.z);
-            a.w = fmaf(w, v.w, a.w);
-        }
-        const float inv = 1.0f / L;
-        o = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    const int64_t base = ((int64_t)s * kQHeads + h) * S;
+    float M = -INFINITY;
+    for (int c = 0; c < S; ++c) M = fmaxf(M, p.ws_ml[base + c].x);
+    float L = 0.0f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < S; ++c) {
+        const float2 ml = p.ws_ml[base + c];
+        const float w = ml.x == -INFINITY ? 0.0f : exp2_fast(ml.x - M);
+        const float4 v = *reinterpret_cast<const float4*>(p.ws_acc + (base + c) * kHeadDim + d4 * 4);
+        L = fmaf(w, ml.y, L);
+        a.x = fmaf(w, v.x, a.x);
+        a.y = fmaf(w, v.y, a.y);
+        a.z = fmaf(w, v.z, a.z);
+        a.w = fmaf(w, v.w, a.w);
     }
-    *reinterpret_cast<float4*>(p.out + s * p.out_stride + h * kHeadDim + d4 * 4) = o;
+    const float inv = L == 0.0f ? 0.0f : 1.0f / L;
+    *reinterpret_cast<float4*>(p.out + s * p.out_stride + h * kHeadDim + d4 * 4) =
+        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(append_kernel, dim3(p.num_seqs), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)p.num_seqs * kAppendBlocksPerSeq),
+                       dim3(kAppendThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream) {
-    const int64_t units = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
-    const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)blocks), dim3(kWavesPerBlock * 64), 0,
+    const int64_t blocks = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
+    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
                        stream, p);
     return hipGetLastError();
 }
