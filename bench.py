@@ -2,16 +2,19 @@
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
-One step = for each of the 16 layers: paged_kv_append (RoPE + page write)
-then paged_decode_attn (split phase + log-sum-exp combine), all on one HIP
-stream, over a seeded synthetic batch already resident in HBM (default: 64
-sequences x 2,048-token context x 16 layers, 4 GiB of KV in one page pool).
-Prints ONE JSON line.  ``value`` is the KV bytes the attention must read per
-step (K and V of every valid token, every layer) divided by the wall time of
-the whole step.  The ``roofline`` entry is for the dominant kernel, the split
-phase, timed with HIP events on the launch stream.  ``cpu_baseline`` is the
-FP64 oracle (append + attention) timed on the host cores over a bounded
-sample of the same workload.
+One step = for each of the 16 layers, the append of the new token (RoPE +
+page write) and the paged decode attention over the cache, over a seeded
+synthetic batch already resident in HBM (default: 64 sequences x 2,048-token
+context x 16 layers, 4 GiB of KV in one page pool).  The timed step issues
+one paged_kv_append_decode_attn per layer (append and attention in one
+launch); the same step as paged_kv_append + paged_decode_attn (two launches
+per layer) is timed beside it.  Prints ONE JSON line.  ``value`` is the KV
+bytes the attention must read per step (K and V of every valid token, every
+layer) divided by the wall time of the whole step.  The ``roofline`` entry
+is for the dominant kernel, the fused append + attention kernel, timed with
+HIP events on the launch stream over back-to-back launches.  ``cpu_baseline``
+is the FP64 oracle (append + attention) timed on the host cores over a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -31,7 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attn: KV-read HBM GB/s (% of MI355X peak); seq·layers/s"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_split_kernel_cfg3_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fused_kernel_cfg3_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_172_amd", "csrc", "kernels.hip")
 
 
@@ -50,6 +53,14 @@ def split_bytes_per_launch(ctx: np.ndarray, splits: int) -> int:
     table = int(pages.sum()) * 4
     outw = ctx.size * (8192 if splits == 1 else splits * 32 * 66 * 4)
     return kv + q + table + outw
+
+
+def append_bytes_per_launch(num_seqs: int) -> int:
+    """Algorithmic bytes the fused kernel adds for the append: the new k and v
+    rows read (8 heads x 64 BF16 each), the K and V rows written to the
+    pages, and the two RoPE table rows (32 FP32 each); q is already counted
+    by the attention."""
+    return num_seqs * (2 * 1024 + 2 * 1024 + 2 * 128)
 
 
 def kernel_source_sha() -> str:
@@ -173,47 +184,55 @@ def main():
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step():
+    def step_fused():
+        for layer in range(L):
+            batch.append_attn(layer, stream)
+
+    def step_unfused():
         for layer in range(L):
             batch.append(layer, stream)
             batch.attn_split(layer, stream)
             batch.attn_combine(layer, stream)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({a.warmup} steps); timing {a.steps} steps")
-    # Pass A: the timed steps (no events inside: an event record costs a few us).
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        """Wall time of reps calls of fn between two events on the stream
+        (no events inside: an event record costs a few microseconds)."""
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    for _ in range(a.warmup):
+        step_unfused()
+        step_fused()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(a.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / a.steps
+    log(f"[bench] warmup done ({a.warmup} steps); timing {a.steps} steps")
+    # The unfused step first: it rotates q in place, which the fused call
+    # then reads as given; repeated appends rewrite the same slot with the
+    # same bits, so every step does identical work.
+    ms_unfused = timed(step_unfused, a.steps)
+    ms_per_step = timed(step_fused, a.steps)
     assert torch.isfinite(batch.out).all(), "non-finite attention output"
-    # Pass B: the dominant kernel alone -- the split phase of every layer,
-    # K times, launched back to back on the same stream between two HIP
-    # events; its average launch duration matches the profiler's kernel time.
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(a.steps):
-        for layer in range(L):
-            batch.attn_split(layer, stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    split_avg = start.elapsed_time(end) / (a.steps * L)
-    split_med = split_avg
+    # The dominant kernel alone, every layer, K times back to back on the
+    # same stream between two HIP events; its average launch duration matches
+    # the profiler's kernel time.  The plain split kernel is timed the same way.
+    fused_avg = timed(lambda: [batch.append_attn(layer, stream) for layer in range(L)], a.steps) / L
+    split_avg = timed(lambda: [batch.attn_split(layer, stream) for layer in range(L)], a.steps) / L
 
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
     splits = batch.splits
     if splits > 1:
-        log("[bench] note: this plan also launches the combine phase; attn_only covers the split phase")
-    alg = split_bytes_per_launch(spec.ctx, splits)
-    achieved = alg / (split_avg * 1e-3) / 1e9
+        log("[bench] note: this plan also launches the combine phase after each split phase")
+    alg_split = split_bytes_per_launch(spec.ctx, splits)
+    alg = alg_split + append_bytes_per_launch(spec.num_seqs)
+    achieved = alg / (fused_avg * 1e-3) / 1e9
     traffic = measured_traffic(splits)
     result = {
         "metric": METRIC,
@@ -233,19 +252,27 @@ def main():
             "num_seqs": spec.num_seqs, "num_layers": L,
             "context_tokens": int(spec.ctx.max()), "pool_pages": spec.num_pages,
             "kv_bytes_per_step": kv_step, "splits": splits, "storage_dtype": "bf16",
+            "step": "paged_kv_append_decode_attn per layer",
             "parallelism": "single GPU",
         },
         "frac_of_peak": round(kv_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "seq_layers_per_s": round(spec.num_seqs * L / (ms_per_step * 1e-3), 1),
+        "unfused_step": {
+            "ms_per_step": round(ms_unfused, 4),
+            "kv_gbps": round(kv_step / (ms_unfused * 1e-3) / 1e9, 2),
+            "calls": "paged_kv_append + paged_decode_attn per layer",
+        },
         "attn_only": {
-            "kv_gbps": round(kv_layer / (split_med * 1e-3) / 1e9, 2),
-            "frac_of_peak": round(kv_layer / (split_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "us_per_layer": round(split_med * 1e3, 2),
-            "seq_layers_per_s": round(spec.num_seqs / (split_med * 1e-3), 1),
+            "kernel": "attn_split_kernel<false>",
+            "kv_gbps": round(kv_layer / (split_avg * 1e-3) / 1e9, 2),
+            "frac_of_peak": round(kv_layer / (split_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "alg_frac_of_peak": round(alg_split / (split_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_per_layer": round(split_avg * 1e3, 2),
+            "seq_layers_per_s": round(spec.num_seqs / (split_avg * 1e-3), 1),
             "combine_launched": splits > 1,
         },
         "roofline": {
-            "kernel": "attn_split_kernel",
+            "kernel": "attn_split_kernel<true> (fused append + attention)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -253,7 +280,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg,
-            "avg_launch_us": round(split_avg * 1e3, 2),
+            "avg_launch_us": round(fused_avg * 1e3, 2),
         },
     }
     if free_stats:

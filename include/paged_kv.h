@@ -107,7 +107,11 @@ int paged_kv_rope_table(double theta, int32_t max_pos, float* cos_out, float* si
  *     BF16 with ties to even; q[s] is overwritten in place;
  *   - rotated K and unchanged V of KV head g go to page
  *     block_table[s*bt_stride + pos/16], slot pos%16.
- * Sequences with n <= 0 are skipped (nothing written).
+ * Sequences with n <= 0 are skipped (nothing written).  A sequence whose
+ * position pos is outside the table (pos >= max_pos) is skipped too (q not
+ * rotated, nothing written); one whose page index pos/16 is at or past
+ * bt_stride, or whose table entry is not a page in [0, num_pages), gets q
+ * rotated but no K/V write.
  *   pool          (host struct, device arrays) the page pool
  *   block_table   (device) int32 [num_seqs][bt_stride], this layer's tables
  *   context_lens  (device) int32 [num_seqs]
@@ -115,8 +119,7 @@ int paged_kv_rope_table(double theta, int32_t max_pos, float* cos_out, float* si
  *   k_new, v_new  (device) BF16 [num_seqs][k_stride / v_stride], heads at g*64
  *   rope_cos/sin  (device) FP32 [max_pos][32] from paged_kv_rope_table
  * q, k_new and v_new may be slices of one packed QKV buffer.
- * Preconditions (unchecked): 1 <= n <= max_pos, the table entry for pos is a
- * page < num_pages, and no two sequences write the same (page, slot).
+ * Precondition (unchecked): no two sequences write the same (page, slot).
  * Errors: INVALID_ARG (null pointer, num_seqs < 0, bt_stride < 1, a stride
  * below its row width, max_pos < 1), ALIGNMENT, HIP.  num_seqs == 0: no-op.
  */
@@ -155,17 +158,17 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
  * block_table[s*bt_stride + t/16], slot t%16.  FP32 online softmax over BF16
  * inputs; the context is cut into chunks (paged_decode_attn_num_splits)
  * whose partial results are merged with the log-sum-exp rule.  Rows with
- * n <= 0 are written as zeros.  Tokens at or past n, pages no table entry
- * below ceil(n/16) names, and table entries at or past ceil(n/16) are
- * never read.
+ * n <= 0 are written as zeros; a length above max_context_len is clamped to
+ * it.  Tokens at or past n, pages no table entry below ceil(n/16) names, and
+ * table entries at or past ceil(n/16) are never read.  A table entry below
+ * ceil(n/16) that is not a page in [0, num_pages) is not dereferenced; that
+ * sequence's rows come out NaN.
  *   max_context_len  host-known upper bound of every context_lens[s] (drives the plan)
  *   q                (device) BF16 [num_seqs][q_stride], already rotated
  *   out              (device) FP32 [num_seqs][out_stride], >= 2048 per row
  *   workspace        (device) >= paged_decode_attn_workspace_size() bytes,
  *                    16-byte aligned; may be NULL when that size is 0.
  *                    Calls running concurrently need separate workspaces.
- * Preconditions (unchecked): 0 <= context_lens[s] <= max_context_len and the
- * table entries below ceil(n/16) are pages < num_pages.
  * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
  * [1, min(2048, 16*bt_stride)], non-finite scale, a stride below its row
  * width), ALIGNMENT (out_stride must be a multiple of 4), WORKSPACE, HIP.
@@ -195,6 +198,32 @@ int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_tabl
 int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
                               int32_t max_context_len, float* out, int64_t out_stride,
                               const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused decode step of one layer: the append and the attention in one
+ * launch ([HN-pool], [HN-attn], [HN-batch]; [TV-decode]: the step is bound
+ * by memory bandwidth, and the append's own launch, with its start-up and
+ * drain, is a visible share of it).  Same result, bit for bit in out (NaN
+ * rows aside: NaN in both, payload unspecified) and in the pool, as
+ *     paged_kv_append(pool, block_table, bt_stride, context_lens, num_seqs,
+ *                     q, q_stride, k_new, k_stride, v_new, v_stride,
+ *                     rope_cos, rope_sin, max_pos, stream);
+ *     paged_decode_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+ *                       max_context_len, q, q_stride, scale, out, out_stride,
+ *                       workspace, workspace_bytes, stream);
+ * except that q is only read: the rotated q is used but not written back.
+ * A new token past max_context_len is still written to its page and, as in
+ * the two calls, not attended.  Arguments, preconditions and errors are
+ * those of the two calls together (the attention's checks come first).
+ * num_seqs == 0: no-op.
+ */
+int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_table,
+                                int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len, const uint16_t* q, int64_t q_stride,
+                                const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                                int64_t v_stride, const float* rope_cos, const float* rope_sin,
+                                int32_t max_pos, float scale, float* out, int64_t out_stride,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Text for a status code; for PKV_ERR_HIP it includes the last HIP error
  * text seen by this thread.  The pointer stays valid until the next call

@@ -28,6 +28,7 @@ EXPORTED = (
     "paged_decode_attn",
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
+    "paged_kv_append_decode_attn",
     "paged_kv_status_string",
 )
 
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_split": ([PP, P, i64, P, i32, i32, P, i64, f32, P, i64, P,
                                      ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_combine": ([P, i32, i32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
+        "paged_kv_append_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64, P, P,
+                                         i32, f32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_kv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -176,3 +179,15 @@ def paged_decode_attn_combine(context_lens, num_seqs, max_context_len, out, out_
     _check(load().paged_decode_attn_combine(
         _p(context_lens), int(num_seqs), int(max_context_len), _p(out), int(out_stride),
         _p(workspace), int(workspace_bytes), _stream(stream)), "paged_decode_attn_combine")
+
+
+def paged_kv_append_decode_attn(pool: Pool, block_table, bt_stride, context_lens, num_seqs,
+                                max_context_len, q, q_stride, k_new, k_stride, v_new, v_stride,
+                                rope_cos, rope_sin, max_pos, scale, out, out_stride,
+                                workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(load().paged_kv_append_decode_attn(
+        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), int(num_seqs),
+        int(max_context_len), _p(q), int(q_stride), _p(k_new), int(k_stride), _p(v_new),
+        int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
+        int(out_stride), _p(workspace), int(workspace_bytes), _stream(stream)),
+        "paged_kv_append_decode_attn")

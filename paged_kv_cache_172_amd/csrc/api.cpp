@@ -74,6 +74,26 @@ int check_pool(const paged_kv_pool* pool) {
     return PKV_OK;
 }
 
+// Checks of the append's own arguments (num_seqs >= 1 checked by the caller).
+int check_append(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                 const int32_t* context_lens, const uint16_t* q, int64_t q_stride,
+                 const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                 int64_t v_stride, const float* rope_cos, const float* rope_sin,
+                 int32_t max_pos) {
+    const int st = check_pool(pool);
+    if (st != PKV_OK) return st;
+    if (!block_table || !context_lens || !q || !k_new || !v_new || !rope_cos || !rope_sin)
+        return PKV_ERR_INVALID_ARG;
+    if (bt_stride < 1 || max_pos < 1) return PKV_ERR_INVALID_ARG;
+    if (q_stride < pkv::kQHeads * pkv::kHeadDim || k_stride < pkv::kKVHeads * pkv::kHeadDim ||
+        v_stride < pkv::kKVHeads * pkv::kHeadDim)
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope_cos) ||
+        !aligned16(rope_sin) || q_stride % 8 || k_stride % 8 || v_stride % 8)
+        return PKV_ERR_ALIGNMENT;
+    return PKV_OK;
+}
+
 struct AttnCheck {
     int status;
     pkv::AttnParams params;
@@ -170,17 +190,9 @@ int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64
                     int32_t max_pos, void* stream) {
     if (num_seqs < 0) return PKV_ERR_INVALID_ARG;
     if (num_seqs == 0) return PKV_OK;
-    const int st = check_pool(pool);
+    const int st = check_append(pool, block_table, bt_stride, context_lens, q, q_stride, k_new,
+                                k_stride, v_new, v_stride, rope_cos, rope_sin, max_pos);
     if (st != PKV_OK) return st;
-    if (!block_table || !context_lens || !q || !k_new || !v_new || !rope_cos || !rope_sin)
-        return PKV_ERR_INVALID_ARG;
-    if (bt_stride < 1 || max_pos < 1) return PKV_ERR_INVALID_ARG;
-    if (q_stride < pkv::kQHeads * pkv::kHeadDim || k_stride < pkv::kKVHeads * pkv::kHeadDim ||
-        v_stride < pkv::kKVHeads * pkv::kHeadDim)
-        return PKV_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope_cos) ||
-        !aligned16(rope_sin) || q_stride % 8 || k_stride % 8 || v_stride % 8)
-        return PKV_ERR_ALIGNMENT;
     pkv::AppendParams p;
     p.k_pool = pool->k_pool;
     p.v_pool = pool->v_pool;
@@ -266,6 +278,36 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
     int st = hip_status(pkv::launch_attn_split(c.params, s));
     if (st != PKV_OK || c.params.plan.splits <= 1) return st;
     return hip_status(pkv::launch_attn_combine(c.params, s));
+}
+
+int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_table,
+                                int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len, const uint16_t* q, int64_t q_stride,
+                                const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                                int64_t v_stride, const float* rope_cos, const float* rope_sin,
+                                int32_t max_pos, float scale, float* out, int64_t out_stride,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+                             max_context_len, q, q_stride, scale, out, out_stride, workspace,
+                             workspace_bytes);
+    if (c.status != PKV_OK || num_seqs == 0) return c.status;
+    const int st = check_append(pool, block_table, bt_stride, context_lens, q, q_stride, k_new,
+                                k_stride, v_new, v_stride, rope_cos, rope_sin, max_pos);
+    if (st != PKV_OK) return st;
+    pkv::AttnParams& p = c.params;
+    p.k_pool_w = pool->k_pool;
+    p.v_pool_w = pool->v_pool;
+    p.k_new = k_new;
+    p.k_stride = k_stride;
+    p.v_new = v_new;
+    p.v_stride = v_stride;
+    p.rope_cos = rope_cos;
+    p.rope_sin = rope_sin;
+    p.max_pos = max_pos;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int ls = hip_status(pkv::launch_append_attn_split(p, s));
+    if (ls != PKV_OK || p.plan.splits <= 1) return ls;
+    return hip_status(pkv::launch_attn_combine(p, s));
 }
 
 const char* paged_kv_status_string(int status) {

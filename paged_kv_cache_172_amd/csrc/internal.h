@@ -60,6 +60,17 @@ struct AttnParams {
     int64_t out_stride;
     float* ws_acc;     // [num_seqs][32][S][64]
     float2* ws_ml;     // [num_seqs][32][S] (maximum in base-2 units, sum)
+    // Fused append only (launch_append_attn_split): the same pool, writable,
+    // the new token's k/v rows and the RoPE table.
+    uint16_t* k_pool_w;
+    uint16_t* v_pool_w;
+    const uint16_t* k_new;
+    int64_t k_stride;
+    const uint16_t* v_new;
+    int64_t v_stride;
+    const float* rope_cos;
+    const float* rope_sin;
+    int32_t max_pos;
 };
 
 Plan make_plan(int32_t num_seqs, int32_t max_context_len);
@@ -67,6 +78,7 @@ size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len);
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream);
+hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);
 
 }  // namespace pkv

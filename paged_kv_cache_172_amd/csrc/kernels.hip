@@ -87,7 +87,7 @@ __device__ __forceinline__ T uniform(T x) {
 
 // Round an FP64 value to the nearest BF16 bit pattern, ties to even, in one
 // step from the FP64 bits (no intermediate FP32 rounding).
-__device__ __noinline__ uint32_t f64_to_bf16_rne_slow(uint64_t u) {
+__device__ __forceinline__ uint32_t f64_to_bf16_rne_slow(uint64_t u) {
     const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
     const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
     if (mag > 0x7FF0000000000000ull) return sign | 0x7FC0u;  // NaN
@@ -394,16 +394,35 @@ __device__ __forceinline__ void ring_round(PageRing& ring, int& j, const uint4 (
     }
 }
 
+// The new token of a fused append: the page that holds it (-1: none in
+// this launch), its slot, and its rotated K and its V row in LDS (BF16
+// pairs, 32 words each).
+struct NewToken {
+    int page;
+    int slot;
+    const uint32_t* k_row;
+    const uint32_t* v_row;
+};
+
 // The last 1..kRing pages of a chunk sit in slots 0..left-1; they are
 // consumed with the slot mask (only the chunk's last page can be partial).
+// The new token, when this launch appends it, is the last valid slot of the
+// sequence's last page and so of a tail; there its slot is masked (what the
+// page held when it was loaded may predate the append), and the wave then
+// consumes the token from LDS in one more masked step.  A masked slot
+// leaves its quad's state bit for bit unchanged, and the token is the last
+// one its quad sees either way, so the result is the one of a separate
+// append followed by the attention.
 template <int I>
 __device__ __forceinline__ void ring_tail(PageRing& ring, int j, int left, int n, int t,
                                           const uint4 (&qa)[kGroup], const uint4 (&qb)[kGroup],
-                                          float sl2, SoftmaxState& st) {
+                                          float sl2, const NewToken& nt, SoftmaxState& st) {
     if constexpr (I < kRing) {
         if (I < left) {
-            consume_page<true>(ring.template at<I>(), qa, qb, sl2, t < n - (j + I) * kPageTokens, st);
-            ring_tail<I + 1>(ring, j, left, n, t, qa, qb, sl2, st);
+            const bool stale = j + I == nt.page && t == nt.slot;
+            consume_page<true>(ring.template at<I>(), qa, qb, sl2,
+                               t < n - (j + I) * kPageTokens && !stale, st);
+            ring_tail<I + 1>(ring, j, left, n, t, qa, qb, sl2, nt, st);
         }
     }
 }
@@ -416,11 +435,27 @@ __device__ __forceinline__ void ring_fill(PageRing& ring, int pb, Issue& issue) 
     }
 }
 
+// Row tasks of the fused append: 6 rows (query heads 4g..4g+3 and the new
+// K of head g, rotated; the new V of head g, copied) x 8 groups of 4 pairs
+// (dims i0..i0+3 and i0+32..i0+35), spread over lanes 0..11 of the 4 waves.
+constexpr int kRotRows = kGroup + 2;
+constexpr int kRotTasksPerWave = kRotRows * 8 / kChunkWaves;
+static_assert(kRotRows * 8 % kChunkWaves == 0, "rotation tasks per wave");
+
+// kFused = false: paged decode attention over the cache as it is (q already
+// rotated by the append).  kFused = true: the same, with the append of the
+// new token done in the same launch: q and the new K are rotated here (the
+// same FP64 rotation and rounding as append_kernel), q is used without being
+// written back, the K/V row is written into its page by the workgroup of
+// outer chunk 0, and the attention reads the new token from registers.
+template <bool kFused>
 __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
 void attn_split_kernel(AttnParams p) {
     // Partials of the workgroup's 4 waves: [wave][head][64 dims] and (max, sum).
     __shared__ float lds_acc[kChunkWaves][kGroup][kHeadDim];
     __shared__ float2 lds_ml[kChunkWaves][kGroup];
+    // Fused append: the new rows (BF16 pairs) [q head 0..3, K, V].
+    __shared__ __align__(16) uint32_t lds_rot[kFused ? kRotRows * kHeadDim / 2 : 4];
 
     const int lane = threadIdx.x & 63;
     const int w = uniform((int)(threadIdx.x >> 6));
@@ -441,13 +476,15 @@ void attn_split_kernel(AttnParams p) {
     const int32_t tbl1 = lane + 64 < bt_w ? bt_row[lane + 64] : 0;
     uint4 qa[kGroup], qb[kGroup];
     const uint16_t* qrow = p.q + (int64_t)s * p.q_stride + (kGroup * g) * kHeadDim;
+    if constexpr (!kFused) {
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-        qa[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + c4 * 8);
-        qb[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + 32 + c4 * 8);
+        for (int r = 0; r < kGroup; ++r) {
+            qa[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + c4 * 8);
+            qb[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + 32 + c4 * 8);
+        }
     }
-    int n = uniform(p.context_lens[s]);
-    n = n < p.max_context_len ? n : p.max_context_len;
+    const int ctx = uniform(p.context_lens[s]);
+    const int n = ctx < p.max_context_len ? ctx : p.max_context_len;
     const int np = n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
 
     // This wave's chunk: the sequence's np pages are cut into 4*S chunks of
@@ -457,20 +494,104 @@ void attn_split_kernel(AttnParams p) {
     const int pb = (kChunkWaves * ci + w) * cs;
     const int pe = min(pb + cs, np);
 
+    // The fused append rotates only where append_kernel would (a token
+    // position inside the RoPE table); otherwise q is used as given.
+    const int pos = ctx - 1;
+    const bool rotate = kFused && ctx >= 1 && pos < p.max_pos;
     float u[16];          // after the wave merge: row R's head, this lane's 16 dims
     float mrow = -INFINITY, lsum = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) u[k] = 0.0f;
     bool bad_page = false;
 
-    if (pb < pe) {
-        const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
-        const uint32_t off_b = off_a + 64;
-        const int32_t tile_bytes = (int32_t)((15 * p.slot_stride + kHeadDim) * 2);
-        const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
-        const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
-        const int64_t page_bytes = p.page_stride * 2;
+    const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
+    const uint32_t off_b = off_a + 64;
+    const int32_t tile_bytes = (int32_t)((15 * p.slot_stride + kHeadDim) * 2);
+    const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
+    const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
+    const int64_t page_bytes = p.page_stride * 2;
 
+    // Issue the loads of logical page j (a no-op load when j >= pe).
+    auto issue = [&](int j) {
+        const bool live = j < pe;
+        const int idx = j < pe - 1 ? j : pe - 1;
+        int32_t phys = idx < 64 ? __builtin_amdgcn_readlane(tbl0, idx)
+                                : __builtin_amdgcn_readlane(tbl1, idx - 64);
+        if (phys < 0 || phys >= p.num_pages) {  // never dereference a bad entry
+            bad_page |= live;
+            phys = 0;
+        }
+        const int32_t bytes = live ? tile_bytes : 0;
+        const int64_t off = (int64_t)phys * page_bytes;
+        return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), off_a,
+                         off_b);
+    };
+
+    // Ring of kRing page buffers: while page j is consumed, pages j+1 ..
+    // j+kRing-1 are in flight.  The last page of the chunk is the only
+    // one that can hold slots past n, so it is consumed with the mask.
+    PageRing ring;
+    NewToken nt;
+    nt.page = -1;
+    nt.slot = -1;
+    nt.k_row = &lds_rot[kGroup * 32];
+    nt.v_row = &lds_rot[(kGroup + 1) * 32];
+    if constexpr (kFused) {
+        // Fused append, part 1: 48 row tasks.  Every lane loads the inputs of
+        // a task (lanes past the 48 repeat the last one) before the first
+        // pages are requested and rotates after that; the task's owner stores
+        // the result in LDS.
+        const int task = min(w * kRotTasksPerWave + lane, kRotRows * 8 - 1);
+        const int row = task >> 3;
+        const int i0 = (task & 7) * 4;
+        const uint16_t* src = row < kGroup ? qrow + row * kHeadDim
+                            : row == kGroup ? p.k_new + (int64_t)s * p.k_stride + g * kHeadDim
+                                            : p.v_new + (int64_t)s * p.v_stride + g * kHeadDim;
+        uint2 x1 = *reinterpret_cast<const uint2*>(src + i0);
+        uint2 x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
+        const int64_t trow = (int64_t)(rotate ? pos : 0) * 32 + i0;
+        const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + trow);
+        const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + trow);
+        // Empty chunks issue no-op loads, so every wave takes the same path.
+        ring_fill<0>(ring, pb, issue);
+        if (rotate && row <= kGroup) rope4(x1, x2, c, sn);
+        if (lane < kRotTasksPerWave) {
+            *reinterpret_cast<uint2*>(&lds_rot[row * 32 + i0 / 2]) = x1;
+            *reinterpret_cast<uint2*>(&lds_rot[row * 32 + 16 + i0 / 2]) = x2;
+        }
+
+        // Fused append, part 2: every wave takes the rotated q rows; outer
+        // chunk 0 stores the new K/V row where append_kernel would.  The
+        // attention reads the new token from LDS when it was appended and
+        // lies inside the attended length.
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kGroup; ++r) {
+            qa[r] = *reinterpret_cast<const uint4*>(&lds_rot[r * 32 + c4 * 4]);
+            qb[r] = *reinterpret_cast<const uint4*>(&lds_rot[r * 32 + 16 + c4 * 4]);
+        }
+        if (rotate && ctx == n) {
+            nt.page = np - 1;
+            nt.slot = pos & (kPageTokens - 1);
+        }
+        if (rotate && ci == 0 && w == 0 && lane < 16) {
+            const int64_t jpage = pos >> 4;
+            if (jpage < p.bt_stride) {
+                const int64_t page = bt_row[jpage];
+                if (page >= 0 && page < p.num_pages) {   // never write through a bad entry
+                    const int64_t dst = page * p.page_stride + g * p.head_stride +
+                                        (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
+                    const int i8 = (lane & 7) * 8;
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        &lds_rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
+                    *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
+                }
+            }
+        }
+    }
+
+    if (pb < pe) {
+        if constexpr (!kFused) ring_fill<0>(ring, pb, issue);
         SoftmaxState st;
 #pragma unroll
         for (int r = 0; r < kGroup; ++r) {
@@ -481,32 +602,21 @@ void attn_split_kernel(AttnParams p) {
         }
         const float sl2 = p.scale_log2;
 
-        // Issue the loads of logical page j (a no-op load when j >= pe).
-        auto issue = [&](int j) {
-            const bool live = j < pe;
-            const int idx = j < pe - 1 ? j : pe - 1;
-            int32_t phys = idx < 64 ? __builtin_amdgcn_readlane(tbl0, idx)
-                                    : __builtin_amdgcn_readlane(tbl1, idx - 64);
-            if (phys < 0 || phys >= p.num_pages) {  // never dereference a bad entry
-                bad_page |= live;
-                phys = 0;
-            }
-            const int32_t bytes = live ? tile_bytes : 0;
-            const int64_t off = (int64_t)phys * page_bytes;
-            return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), off_a,
-                             off_b);
-        };
-
-        // Ring of kRing page buffers: while page j is consumed, pages j+1 ..
-        // j+kRing-1 are in flight.  The last page of the chunk is the only
-        // one that can hold slots past n, so it is consumed with the mask.
-        PageRing ring;
-        ring_fill<0>(ring, pb, issue);
         int j = pb;
         const int rounds = (pe - 1 - pb) / kRing;   // whole rounds of unmasked pages
         for (int r = 0; r < rounds; ++r) ring_round<0>(ring, j, qa, qb, sl2, st, issue);
         ring.template at<kRing - 1>() = issue(j + kRing - 1);
-        ring_tail<0>(ring, j, pe - j, n, t, qa, qb, sl2, st);
+        ring_tail<0>(ring, j, pe - j, n, t, qa, qb, sl2, nt, st);
+        if constexpr (kFused) {
+            if (nt.page >= pb && nt.page < pe) {
+                PageRegs pg;
+                pg.ka = *reinterpret_cast<const uint4*>(nt.k_row + c4 * 4);
+                pg.kb = *reinterpret_cast<const uint4*>(nt.k_row + 16 + c4 * 4);
+                pg.va = *reinterpret_cast<const uint4*>(nt.v_row + c4 * 4);
+                pg.vb = *reinterpret_cast<const uint4*>(nt.v_row + 16 + c4 * 4);
+                consume_page<true>(pg, qa, qb, sl2, t == nt.slot, st);
+            }
+        }
 
         // ---- merge the 16 quads of the wave (log-sum-exp rule) ----
         float M[kGroup];
@@ -633,7 +743,14 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 
 hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
-    hipLaunchKernelGGL(attn_split_kernel, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
+    hipLaunchKernelGGL(attn_split_kernel<false>, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream) {
+    const int64_t blocks = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
+    hipLaunchKernelGGL(attn_split_kernel<true>, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
                        stream, p);
     return hipGetLastError();
 }

@@ -110,8 +110,21 @@ class DecodeBatch:
             self.context_lens, self.num_seqs, self.max_context_len, self.out[layer], Q_ROW,
             self.workspace, self.ws_bytes, self._stream(stream))
 
+    def append_attn(self, layer: int, stream=None) -> None:
+        """The fused append + attention of one layer (q is left unrotated)."""
+        _lib.paged_kv_append_decode_attn(
+            self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
+            self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.k[layer], KV_ROW,
+            self.v[layer], KV_ROW, self.rope_cos, self.rope_sin, self.max_pos, self.scale,
+            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream))
+
     def step(self, stream=None) -> None:
         """One decode step: for every layer, append then attention."""
         for layer in range(self.num_layers):
             self.append(layer, stream)
             self.attn(layer, stream)
+
+    def step_fused(self, stream=None) -> None:
+        """One decode step with the fused call per layer."""
+        for layer in range(self.num_layers):
+            self.append_attn(layer, stream)

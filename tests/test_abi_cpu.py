@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -202,3 +202,35 @@ def test_combine_rejects(lib):
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(pkv.status_string(code), str) and pkv.status_string(code)
+
+
+FUSED_CASES = [
+    ({"k_new": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"rope_cos": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"max_pos": 0}, pkv.PKV_ERR_INVALID_ARG),
+    ({"k_stride": 256}, pkv.PKV_ERR_INVALID_ARG),
+    ({"v_new": FAKE + 8}, pkv.PKV_ERR_ALIGNMENT),
+    ({"rope_sin": FAKE + 4}, pkv.PKV_ERR_ALIGNMENT),
+    ({"q": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"max_context_len": 2049}, pkv.PKV_ERR_INVALID_ARG),
+    ({"scale": float("nan")}, pkv.PKV_ERR_INVALID_ARG),
+    ({"out": FAKE + 4}, pkv.PKV_ERR_ALIGNMENT),
+    ({"workspace_bytes": 100}, pkv.PKV_ERR_WORKSPACE),
+    ({"num_seqs": -1}, pkv.PKV_ERR_INVALID_ARG),
+    ({"num_seqs": 0}, pkv.PKV_OK),
+]
+
+
+@pytest.mark.parametrize("kw,want", FUSED_CASES)
+def test_fused_rejects(lib, kw, want):
+    a = dict(block_table=FAKE, bt_stride=128, context_lens=FAKE, num_seqs=4, max_context_len=2048,
+             q=FAKE, q_stride=Q_ROW, k_new=FAKE, k_stride=KV_ROW, v_new=FAKE, v_stride=KV_ROW,
+             rope_cos=FAKE, rope_sin=FAKE, max_pos=2048, scale=0.125, out=FAKE, out_stride=Q_ROW,
+             workspace=FAKE, workspace_bytes=1 << 30)
+    a.update(kw)
+    try:
+        pkv.paged_kv_append_decode_attn(_pool(), **a)
+        got = pkv.PKV_OK
+    except pkv.PagedKVError as e:
+        got = e.status
+    assert got == want

@@ -1,0 +1,152 @@
+"""GPU parity of the fused call paged_kv_append_decode_attn.
+
+It must give, bit for bit, the output and the pool of paged_kv_append
+followed by paged_decode_attn on the same inputs (both checked against the
+FP64 oracle elsewhere), leave q unrotated, and meet the oracle's attention
+tolerance on its own.  Edge cases: new tokens past max_context_len, positions
+outside the RoPE table, a bad page id for the new token, empty rows, and the
+split + combine plan.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import PoolView
+import paged_kv_cache_172_amd as pkv
+from paged_kv_cache_172_amd import pages as pg
+from paged_kv_cache_172_amd import workload as wl
+from paged_kv_cache_172_amd.runner import DecodeBatch
+
+from tests.gpu_util import assert_attn_close, host_batch, say, to_u16
+from tests.test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU (run with -m 'not gpu' on CPU)"
+    pkv.load()
+    return torch
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.fixture(scope="module")
+def rope(orc):
+    return orc.rope_table(500000.0, 2048)
+
+
+def same_bits(torch, a, b) -> bool:
+    """Bitwise equality of two tensors; for FP32, NaN must sit in the same
+    places in both (its payload may differ: a row that reads a bad page id
+    is NaN whichever way the NaN arose)."""
+    if a.dtype != torch.float32:
+        return bool(torch.equal(a, b))
+    na, nb = torch.isnan(a), torch.isnan(b)
+    if not torch.equal(na, nb):
+        return False
+    keep = ~na
+    return bool(torch.equal(a[keep].view(torch.int32), b[keep].view(torch.int32)))
+
+
+def run_both(torch, make_batch, num_layers):
+    """Two batches built from the same inputs: append + attention on one,
+    the fused call on the other."""
+    sep, fus = make_batch(), make_batch()
+    q_before = fus.q.clone()
+    for layer in range(num_layers):
+        sep.append(layer)
+        sep.attn(layer)
+        fus.append_attn(layer)
+    torch.cuda.synchronize()
+    assert same_bits(torch, fus.q, q_before), "the fused call must leave q as given"
+    return sep, fus
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_equals_append_then_attn(torch_gpu, rope, name):
+    torch = torch_gpu
+    spec = SMALL[name]()
+    hw = wl.make_host_workload(spec)
+    sep, fus = run_both(torch, lambda: host_batch(hw, rope), spec.num_layers)
+    say(f"[fused] {name}: B={spec.num_seqs} L={spec.num_layers} splits={fus.splits}")
+    assert same_bits(torch, fus.out, sep.out), "output differs from append + attention"
+    assert same_bits(torch, fus.pool_pages, sep.pool_pages), "pool differs from append"
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "edges"])
+def test_fused_matches_oracle(torch_gpu, orc, rope, name):
+    spec = SMALL[name]()
+    hw = wl.make_host_workload(spec)
+    batch = host_batch(hw, rope)
+    for layer in range(spec.num_layers):
+        batch.append_attn(layer)
+    out = batch.out.cpu().numpy()
+    pages = hw.pages.copy()
+    q = hw.q.copy()
+    for layer in range(spec.num_layers):
+        bt = np.ascontiguousarray(spec.block_tables[layer])
+        orc.append(PoolView.from_pages(pages), bt, spec.ctx, q[layer],
+                   np.ascontiguousarray(hw.k[layer]), np.ascontiguousarray(hw.v[layer]),
+                   rope[0], rope[1])
+        ref = orc.attn(PoolView.from_pages(pages), bt, spec.ctx, np.ascontiguousarray(q[layer]),
+                       0.125)
+        assert_attn_close(out[layer], ref, f"fused {name} layer {layer}")
+    assert np.array_equal(to_u16(batch.pool_pages).reshape(pages.shape), pages)
+
+
+def test_fused_edge_cases(torch_gpu, rope):
+    """Lengths past max_context_len (written, not attended), positions past
+    the RoPE table (not rotated, not written), a bad page id for one new
+    token (NaN row, nothing written) and an empty row."""
+    torch = torch_gpu
+    lengths = [40, 70, 100, 33, 1, 64]
+    spec = wl.make_spec(lengths, 1, seed=520)
+    hw = wl.make_host_workload(spec)
+    ctx = spec.ctx.copy()
+    ctx[4] = 0                                   # empty row
+    bt = spec.block_tables.copy()
+    bt[0, 3, (33 - 1) // 16] = spec.num_pages + 3   # new token's page id out of range
+    short_rope = (rope[0][:90].copy(), rope[1][:90].copy())   # positions >= 90 not in the table
+
+    def make():
+        return DecodeBatch(hw.pages, bt, ctx, hw.q, hw.k, hw.v, rope=short_rope,
+                           max_context_len=64)
+    sep, fus = run_both(torch, make, 1)
+    assert same_bits(torch, fus.out, sep.out)
+    assert same_bits(torch, fus.pool_pages, sep.pool_pages)
+    out = fus.out[0].cpu().numpy()
+    assert np.isnan(out[3]).all() and not out[4].any()
+    assert np.isfinite(out[[0, 1, 2, 5]]).all()
+
+
+@pytest.mark.parametrize("k", [3, 4, 5])
+def test_fused_full_size_equals_append_then_attn(torch_gpu, rope, k):
+    """The full-size configurations in the launch configuration the benchmark
+    times: the fused call against append + attention on a copy of the pool."""
+    torch = torch_gpu
+    spec = wl.config_spec(k)
+    pool = wl.make_device_pool(spec)
+    q, kk, v = wl.draw_new_tokens(spec)
+    bt = spec.block_tables.copy()
+    if len(spec.crossers):
+        pg.lazy_page_step(bt, spec.ctx, pg.FreeList(spec.free_pages, spec.num_pages))
+    sep = DecodeBatch(pool, bt, spec.ctx, q, kk, v, rope=rope, max_context_len=2048)
+    fus = DecodeBatch(pool.clone(), bt, spec.ctx, q, kk, v, rope=rope, max_context_len=2048)
+    del pool
+    say(f"[fused full] config {k}: B={spec.num_seqs} L={spec.num_layers} splits={fus.splits}")
+    q_before = fus.q.clone()
+    sep.step()
+    fus.step_fused()
+    torch.cuda.synchronize()
+    assert torch.isfinite(fus.out).all()
+    assert same_bits(torch, fus.out, sep.out)
+    assert same_bits(torch, fus.pool_pages, sep.pool_pages)
+    assert same_bits(torch, fus.q, q_before)
+    del sep, fus
+    torch.cuda.empty_cache()
