@@ -437,10 +437,12 @@ __device__ __forceinline__ void ring_fill(PageRing& ring, int pb, Issue& issue) 
 
 // Row tasks of the fused append: 6 rows (query heads 4g..4g+3 and the new
 // K of head g, rotated; the new V of head g, copied) x 8 groups of 4 pairs
-// (dims i0..i0+3 and i0+32..i0+35), spread over lanes 0..11 of the 4 waves.
+// (dims i0..i0+3 and i0+32..i0+35).  Every wave runs all 48 in its lanes
+// 0..47 and passes the rows to its other lanes through its own LDS rows, so
+// no wave waits for another.
 constexpr int kRotRows = kGroup + 2;
-constexpr int kRotTasksPerWave = kRotRows * 8 / kChunkWaves;
-static_assert(kRotRows * 8 % kChunkWaves == 0, "rotation tasks per wave");
+constexpr int kRotTasks = kRotRows * 8;
+static_assert(kRotTasks <= 64, "one task per lane");
 
 // kFused = false: paged decode attention over the cache as it is (q already
 // rotated by the append).  kFused = true: the same, with the append of the
@@ -454,8 +456,8 @@ void attn_split_kernel(AttnParams p) {
     // Partials of the workgroup's 4 waves: [wave][head][64 dims] and (max, sum).
     __shared__ float lds_acc[kChunkWaves][kGroup][kHeadDim];
     __shared__ float2 lds_ml[kChunkWaves][kGroup];
-    // Fused append: the new rows (BF16 pairs) [q head 0..3, K, V].
-    __shared__ __align__(16) uint32_t lds_rot[kFused ? kRotRows * kHeadDim / 2 : 4];
+    // Fused append: each wave's new rows (BF16 pairs) [q head 0..3, K, V].
+    __shared__ __align__(16) uint32_t lds_rot[kFused ? kChunkWaves : 1][kRotRows * kHeadDim / 2];
 
     const int lane = threadIdx.x & 63;
     const int w = uniform((int)(threadIdx.x >> 6));
@@ -534,14 +536,14 @@ void attn_split_kernel(AttnParams p) {
     NewToken nt;
     nt.page = -1;
     nt.slot = -1;
-    nt.k_row = &lds_rot[kGroup * 32];
-    nt.v_row = &lds_rot[(kGroup + 1) * 32];
+    uint32_t* rot = lds_rot[kFused ? w : 0];
+    nt.k_row = rot + kGroup * 32;
+    nt.v_row = rot + (kGroup + 1) * 32;
     if constexpr (kFused) {
-        // Fused append, part 1: 48 row tasks.  Every lane loads the inputs of
-        // a task (lanes past the 48 repeat the last one) before the first
-        // pages are requested and rotates after that; the task's owner stores
-        // the result in LDS.
-        const int task = min(w * kRotTasksPerWave + lane, kRotRows * 8 - 1);
+        // Fused append, part 1: the 48 row tasks, one per lane (lanes past
+        // 47 repeat the last one).  Their inputs are requested before the
+        // first pages and the rotation runs while those are in flight.
+        const int task = min(lane, kRotTasks - 1);
         const int row = task >> 3;
         const int i0 = (task & 7) * 4;
         const uint16_t* src = row < kGroup ? qrow + row * kHeadDim
@@ -555,20 +557,24 @@ void attn_split_kernel(AttnParams p) {
         // Empty chunks issue no-op loads, so every wave takes the same path.
         ring_fill<0>(ring, pb, issue);
         if (rotate && row <= kGroup) rope4(x1, x2, c, sn);
-        if (lane < kRotTasksPerWave) {
-            *reinterpret_cast<uint2*>(&lds_rot[row * 32 + i0 / 2]) = x1;
-            *reinterpret_cast<uint2*>(&lds_rot[row * 32 + 16 + i0 / 2]) = x2;
+        if (lane < kRotTasks) {
+            *reinterpret_cast<uint2*>(&rot[row * 32 + i0 / 2]) = x1;
+            *reinterpret_cast<uint2*>(&rot[row * 32 + 16 + i0 / 2]) = x2;
         }
 
-        // Fused append, part 2: every wave takes the rotated q rows; outer
+        // Fused append, part 2: the wave's lanes take the rotated q rows
+        // (LDS ops of one wave complete in order; the fences keep the
+        // compiler from moving the reads above the writes); wave 0 of outer
         // chunk 0 stores the new K/V row where append_kernel would.  The
         // attention reads the new token from LDS when it was appended and
         // lies inside the attended length.
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int r = 0; r < kGroup; ++r) {
-            qa[r] = *reinterpret_cast<const uint4*>(&lds_rot[r * 32 + c4 * 4]);
-            qb[r] = *reinterpret_cast<const uint4*>(&lds_rot[r * 32 + 16 + c4 * 4]);
+            qa[r] = *reinterpret_cast<const uint4*>(&rot[r * 32 + c4 * 4]);
+            qb[r] = *reinterpret_cast<const uint4*>(&rot[r * 32 + 16 + c4 * 4]);
         }
         if (rotate && ctx == n) {
             nt.page = np - 1;
@@ -583,7 +589,7 @@ void attn_split_kernel(AttnParams p) {
                                         (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
                     const int i8 = (lane & 7) * 8;
                     const uint4 val = *reinterpret_cast<const uint4*>(
-                        &lds_rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
+                        &rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
                     *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
                 }
             }
