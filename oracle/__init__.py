@@ -105,6 +105,9 @@ class Oracle:
         lib.pkv_oracle_append.argtypes = [
             P, P, i64, i64, i64, i64, P, i64, P, i32, P, i64, P, i64, P, i64, P, P, i32]
         lib.pkv_oracle_append.restype = ctypes.c_int
+        lib.pkv_oracle_prefill.argtypes = [
+            P, P, i64, i64, i64, i64, P, i64, P, P, i32, P, i64, P, i64, P, i64, P, P, i32]
+        lib.pkv_oracle_prefill.restype = ctypes.c_int
         lib.pkv_oracle_attn.argtypes = [
             P, P, i64, i64, i64, i64, P, i64, P, i32, P, i64, dbl, P, i64, P, i64]
         lib.pkv_oracle_attn.restype = ctypes.c_int
@@ -173,6 +176,30 @@ class Oracle:
             _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0])
         if rc != 0:
             raise ValueError(f"oracle append failed ({rc})")
+
+    def prefill(self, pool: PoolView, block_table, start_pos, cu_tokens, q, k, v, rope_cos,
+                rope_sin) -> None:
+        """In place: the prompt rows of every sequence appended token by token.
+
+        block_table int32 [B][bt_stride]; start_pos int32 [B]; cu_tokens int32
+        [B+1]; q uint16 [T][q_stride] or None; k, v uint16 [T][stride]."""
+        _req(block_table, np.int32, "block_table")
+        _req(start_pos, np.int32, "start_pos")
+        _req(cu_tokens, np.int32, "cu_tokens")
+        for a, n in ((k, "k"), (v, "v")):
+            _req(a, np.uint16, n)
+        if q is not None:
+            _req(q, np.uint16, "q")
+        _req(rope_cos, np.float32, "rope_cos")
+        _req(rope_sin, np.float32, "rope_sin")
+        rc = self.lib.pkv_oracle_prefill(
+            _ptr(pool.k), _ptr(pool.v), pool.num_pages, pool.page_stride, pool.head_stride,
+            pool.slot_stride, _ptr(block_table), block_table.shape[1], _ptr(start_pos),
+            _ptr(cu_tokens), start_pos.shape[0], _ptr(q) if q is not None else None,
+            q.shape[1] if q is not None else 0, _ptr(k), k.shape[1], _ptr(v), v.shape[1],
+            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0])
+        if rc != 0:
+            raise ValueError(f"oracle prefill failed ({rc})")
 
     def attn(self, pool: PoolView, block_table, ctx, q, scale: float, want64: bool = False):
         """FP32 output [B][32*64] (and the FP64 output when want64)."""

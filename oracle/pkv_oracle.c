@@ -192,6 +192,40 @@ int pkv_oracle_append(uint16_t* k_pool, uint16_t* v_pool, int64_t num_pages, int
     return 0;
 }
 
+/* Prefill page fill ("Hours of YouTube and 85 handtyped pages of notes on LLM
+ * Inference - Start here", section "これまでの進捗", page-pool bullet: the
+ * prefill fills the prompt's pages).  The prompt rows are packed: sequence s
+ * owns rows cu_tokens[s] .. cu_tokens[s+1]-1, and its row i is the token at
+ * position start_pos[s] + i.  The fill is defined as the decode append of
+ * each token in turn, with context length = its position + 1.  q may be NULL
+ * (then only K/V are written).  Returns 0, or the first append's error. */
+int pkv_oracle_prefill(uint16_t* k_pool, uint16_t* v_pool, int64_t num_pages, int64_t page_stride,
+                       int64_t head_stride, int64_t slot_stride, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* start_pos, const int32_t* cu_tokens,
+                       int32_t num_seqs, uint16_t* q, int64_t q_stride, const uint16_t* k,
+                       int64_t k_stride, const uint16_t* v, int64_t v_stride,
+                       const float* rope_cos, const float* rope_sin, int32_t max_pos) {
+    uint16_t scratch_q[HQ * HD];
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        for (int32_t row = cu_tokens[s]; row < cu_tokens[s + 1]; ++row) {
+            const int32_t n = start_pos[s] + (row - cu_tokens[s]) + 1;
+            uint16_t* qrow = scratch_q;
+            if (q) {
+                qrow = q + (int64_t)row * q_stride;
+            } else {
+                memset(scratch_q, 0, sizeof scratch_q);
+            }
+            const int rc = pkv_oracle_append(
+                k_pool, v_pool, num_pages, page_stride, head_stride, slot_stride,
+                block_table + (int64_t)s * bt_stride, bt_stride, &n, 1, qrow, HQ * HD,
+                k + (int64_t)row * k_stride, k_stride, v + (int64_t)row * v_stride, v_stride,
+                rope_cos, rope_sin, max_pos);
+            if (rc != 0) return rc;
+        }
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------- attention -- */
 
 /* out64 (may be NULL) and out32 (may be NULL) are [num_seqs][32*64] rows with

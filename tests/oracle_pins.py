@@ -248,6 +248,98 @@ def pin_append_unit_vectors(o: Oracle):
         assert int(qh[i]) == c_bits and int(qh[i + 32]) == s_bits
 
 
+# --------------------------------------------------------------- prefill --
+
+def _prefill_case(seed, starts, counts, extra_pages=4):
+    """Tables, packed rows and a poisoned pool for prompts of `counts` tokens
+    that start at positions `starts`."""
+    rng = np.random.default_rng(seed)
+    B = len(starts)
+    need = [-(-(st + c) // 16) for st, c in zip(starts, counts)]
+    num_pages = sum(need) + extra_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((B, 128), -1, np.int32)
+    cur = 0
+    for s_, c in enumerate(need):
+        bt[s_, :c] = perm[cur:cur + c]
+        cur += c
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(counts)
+    T = int(cu[-1])
+    q = wl.f32_to_bf16_bits(rng.standard_normal((T, H * D)))
+    k = wl.f32_to_bf16_bits(rng.standard_normal((T, G * D)))
+    v = wl.f32_to_bf16_bits(rng.standard_normal((T, G * D)))
+    return bt, np.asarray(starts, np.int32), cu, q, k, v, num_pages
+
+
+def pin_prefill_equals_sequential_appends(o: Oracle):
+    """The fill equals the (separately pinned) append of each prompt token in
+    turn, with context length position + 1: pool and rotated q, bit for bit."""
+    cos, sin = o.rope_table(THETA, 2048)
+    bt, st, cu, q, k, v, P = _prefill_case(60, [0, 5, 30, 2040], [20, 1, 40, 8])
+    pages = _blank_pool(P, fill_seed=61)
+    ref = pages.copy()
+    q_ref = q.copy()
+    q_fill = q.copy()
+    o.prefill(PoolView.from_pages(pages), bt, st, cu, q_fill, k, v, cos, sin)
+    for s_ in range(len(st)):
+        for row in range(cu[s_], cu[s_ + 1]):
+            n = np.array([st[s_] + (row - cu[s_]) + 1], np.int32)
+            o.append(PoolView.from_pages(ref), np.ascontiguousarray(bt[s_:s_ + 1]), n,
+                     q_ref[row:row + 1], np.ascontiguousarray(k[row:row + 1]),
+                     np.ascontiguousarray(v[row:row + 1]), cos, sin)
+    assert np.array_equal(pages, ref) and np.array_equal(q_fill, q_ref)
+    # without q, the same pool
+    pages2 = _blank_pool(P, fill_seed=61)
+    o.prefill(PoolView.from_pages(pages2), bt, st, cu, None, k, v, cos, sin)
+    assert np.array_equal(pages2, ref)
+
+
+def pin_prefill_writes_exactly_the_prompt_slots(o: Oracle):
+    """Exactly the slots of positions start .. start+count-1 change, at page
+    bt[pos div 16], slot pos mod 16; V is copied; the token at position 0 keeps
+    its K (rotation by angle 0)."""
+    cos, sin = o.rope_table(THETA, 2048)
+    starts, counts = [0, 17, 3], [33, 15, 1]
+    bt, st, cu, q, k, v, P = _prefill_case(62, starts, counts)
+    pages = _blank_pool(P, fill_seed=63)
+    before = pages.copy()
+    o.prefill(PoolView.from_pages(pages), bt, st, cu, None, k, v, cos, sin)
+    expect = np.zeros(pages.shape, bool)
+    for s_, (a, c) in enumerate(zip(starts, counts)):
+        for i in range(c):
+            pos = a + i
+            p = bt[s_, pos // 16]
+            expect[p, :, :, pos % 16, :] = True
+            row = cu[s_] + i
+            assert np.array_equal(pages[p, 1, :, pos % 16, :], v[row].reshape(G, D))
+            if pos == 0:
+                assert np.array_equal(pages[p, 0, :, 0, :], k[row].reshape(G, D))
+    assert not ((pages != before) & ~expect).any()
+
+
+def pin_prefill_then_attention_bruteforce(o: Oracle):
+    """A 37-token prompt filled at positions 0..36, then attention with
+    ctx = 37, equals dense attention over keys rotated here with the
+    (separately pinned) FP64 rotation and the library BF16 rounding."""
+    cos, sin = o.rope_table(THETA, 2048)
+    bt, st, cu, q, k, v, P = _prefill_case(64, [0], [37])
+    pages = _blank_pool(P)
+    o.prefill(PoolView.from_pages(pages), bt, st, cu, None, k, v, cos, sin)
+    kk = np.empty((37, G, D), np.uint16)
+    for pos in range(37):
+        for g in range(G):
+            x = bf16_to_f64(k[pos].reshape(G, D)[g])
+            y = o.rope_rotate_f64(x, cos[pos], sin[pos])
+            kk[pos, g] = o.bf16_round_array(y)
+    vv = v.reshape(37, G, D)
+    qq = q[36:37].copy()
+    _, out = o.attn(PoolView.from_pages(pages), bt, np.array([37], np.int32), qq, SCALE, True)
+    for h in (0, 13, 31):
+        want = _brute(qq[0, h * D:(h + 1) * D], kk, vv, h // 4)
+        assert np.allclose(out[0, h * D:(h + 1) * D], want, rtol=0, atol=1e-12), h
+
+
 # ------------------------------------------------------------- attention --
 
 def _single_seq_pool(kv_k, kv_v, seed=0, pool_pages=None):

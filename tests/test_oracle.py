@@ -61,6 +61,10 @@ MUTATIONS = {
     "bf16_precision": ("double spacing = ldexp(1.0, binade - 7);", "double spacing = ldexp(1.0, binade - 8);"),
     "bf16_subnormal_clamp": ("if (binade < -126) binade = -126;", ""),
     "q_not_rotated": ("memcpy(qh, rotated, sizeof rotated);", ""),
+    "prefill_position_off_by_one": ("const int32_t n = start_pos[s] + (row - cu_tokens[s]) + 1;",
+                                    "const int32_t n = start_pos[s] + (row - cu_tokens[s]);"),
+    "prefill_row_of_first_sequence": ("k + (int64_t)row * k_stride, k_stride,",
+                                      "k + (int64_t)(row - cu_tokens[s]) * k_stride, k_stride,"),
     "k_from_q_row": ("const uint16_t* kg = k + (int64_t)s * k_stride + (int64_t)g * HD;",
                      "const uint16_t* kg = k + (int64_t)s * k_stride + (int64_t)(g / 2) * HD;"),
 }
