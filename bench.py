@@ -63,6 +63,64 @@ def append_bytes_per_launch(num_seqs: int) -> int:
     return num_seqs * (2 * 1024 + 2 * 1024 + 2 * 128)
 
 
+PREFILL_SEQS, PREFILL_TOKENS = 64, 2048
+
+
+def prefill_bytes_per_token(with_q: bool) -> int:
+    """Algorithmic bytes of the prefill fill per prompt token: k and v rows
+    read (1 KiB each), K' and V rows written into the pages (1 KiB each), the
+    two RoPE table rows (128 B each) and, with q, its row read and written
+    back (4 KiB each)."""
+    return 4 * 1024 + 256 + (8 * 1024 if with_q else 0)
+
+
+def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
+    """The prefill page fill of 64 prompts x 2,048 tokens (one layer, q
+    rotated) into a 256 MiB pool of its own, shuffled; average launch time
+    from HIP events around back-to-back launches."""
+    from paged_kv_cache_172_amd.runner import HALF_PAGE, PAGE_ELEMS
+    dev = torch.device("cuda", 0)
+    B, n = PREFILL_SEQS, PREFILL_TOKENS
+    T = B * n
+    P = T // 16
+    g = torch.Generator(device=dev).manual_seed(172100)
+    pages = torch.empty((P, 2, 8, 16, 64), dtype=torch.int16, device=dev)
+    perm = torch.randperm(P, generator=g, device=dev).to(torch.int32)
+    bt = perm.view(B, 128).contiguous()
+    start = torch.zeros(B, dtype=torch.int32, device=dev)
+    cu = (torch.arange(B + 1, device=dev, dtype=torch.int32) * n).contiguous()
+    rows = lambda c: torch.randn((T, c), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    q, k, v = rows(2048), rows(512), rows(512)
+    base = pages.data_ptr()
+    pool = pkv.make_pool(base, base + HALF_PAGE * 2, P, PAGE_ELEMS, 1024, 64)
+
+    def launch():
+        pkv.paged_kv_prefill(pool, bt, 128, start, cu, B, T, q, 2048, k, 512, v, 512,
+                             rope_cos, rope_sin, rope_cos.shape[0], stream)
+
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    alg = T * prefill_bytes_per_token(True)
+    gbps = alg / (us * 1e-6) / 1e9
+    return {
+        "workload": f"{B} prompts x {n} tokens, one layer, q rotated in place",
+        "kernel": "append_kernel<true> (paged_kv_prefill)",
+        "us_per_launch": round(us, 2),
+        "tokens_per_s": round(T / (us * 1e-6), 1),
+        "algorithmic_bytes_per_launch": alg,
+        "gbps": round(gbps, 1),
+        "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+    }
+
+
 def kernel_source_sha() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -225,6 +283,8 @@ def main():
     fused_avg = timed(lambda: [batch.append_attn(layer, stream) for layer in range(L)], a.steps) / L
     split_avg = timed(lambda: [batch.attn_split(layer, stream) for layer in range(L)], a.steps) / L
 
+    prefill = time_prefill(torch, pkv, stream, batch.rope_cos, batch.rope_sin, max(3, a.steps // 2))
+
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
     splits = batch.splits
@@ -283,6 +343,7 @@ def main():
             "avg_launch_us": round(fused_avg * 1e3, 2),
         },
     }
+    result["prefill_fill"] = prefill
     if free_stats:
         result["free_list"] = free_stats
     if not a.no_cpu_baseline:

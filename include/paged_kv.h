@@ -130,6 +130,39 @@ int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64
                     int32_t max_pos, void* stream);
 
 /*
+ * Prefill page fill ([HN-pool]: the prefill fills the prompt's pages, which
+ * decode then extends one token at a time).  Prompt rows are packed: the
+ * rows of sequence s are cu_tokens[s] .. cu_tokens[s+1]-1, and its row i is
+ * the token at position start_pos[s] + i (start_pos[s] = tokens it already
+ * holds, 0 for a fresh prompt; several sequences and chunked prompts share
+ * one call).  Each row is handled exactly as paged_kv_append handles a
+ * sequence with context length position + 1: its q (if q is not NULL) and k
+ * are rotated at its position and rounded once to BF16, q in place, and K'
+ * and V go to page block_table[s*bt_stride + position/16], slot position%16.
+ * The result equals the appends of the rows one after another, bit for bit.
+ * The same guards apply per row: a position outside the RoPE table skips the
+ * row, a page index at or past bt_stride or a table entry outside
+ * [0, num_pages) skips its K/V write.
+ *   start_pos   (device) int32 [num_seqs]
+ *   cu_tokens   (device) int32 [num_seqs + 1], non-decreasing, cu_tokens[0] = 0
+ *               and cu_tokens[num_seqs] = total_tokens
+ *   total_tokens host copy of cu_tokens[num_seqs] (sizes the launch)
+ *   q           (device) BF16 [total_tokens][q_stride] or NULL
+ *   k_new, v_new (device) BF16 [total_tokens][k_stride / v_stride]
+ * Preconditions (unchecked): the offsets are as stated, and no two rows write
+ * the same (page, slot).
+ * Errors: INVALID_ARG (null pointer other than q, negative counts,
+ * total_tokens > 2^30, bt_stride < 1, a stride below its row width,
+ * max_pos < 1), ALIGNMENT, HIP.  num_seqs == 0 or total_tokens == 0: no-op.
+ */
+int paged_kv_prefill(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* start_pos, const int32_t* cu_tokens, int32_t num_seqs,
+                     int32_t total_tokens, uint16_t* q, int64_t q_stride, const uint16_t* k_new,
+                     int64_t k_stride, const uint16_t* v_new, int64_t v_stride,
+                     const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                     void* stream);
+
+/*
  * Split plan of the decode attention.  Each (sequence, KV head) is served by
  * S workgroups of 4 wavefronts.  A sequence whose context fills np pages is
  * cut into 4*S chunks of ceil(np / (4*S)) whole pages, in logical order; each

@@ -29,6 +29,7 @@ EXPORTED = (
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
     "paged_kv_append_decode_attn",
+    "paged_kv_prefill",
     "paged_kv_status_string",
 )
 
@@ -79,6 +80,8 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_combine": ([P, i32, i32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_kv_append_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64, P, P,
                                          i32, f32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
+        "paged_kv_prefill": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P, P, i32, P],
+                             ctypes.c_int),
         "paged_kv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -191,3 +194,14 @@ def paged_kv_append_decode_attn(pool: Pool, block_table, bt_stride, context_lens
         int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
         int(out_stride), _p(workspace), int(workspace_bytes), _stream(stream)),
         "paged_kv_append_decode_attn")
+
+
+def paged_kv_prefill(pool: Pool, block_table, bt_stride, start_pos, cu_tokens, num_seqs,
+                     total_tokens, q, q_stride, k_new, k_stride, v_new, v_stride, rope_cos,
+                     rope_sin, max_pos, stream=None) -> None:
+    """q may be None (K/V only)."""
+    _check(load().paged_kv_prefill(
+        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(start_pos), _p(cu_tokens),
+        int(num_seqs), int(total_tokens), _p(q), int(q_stride), _p(k_new), int(k_stride),
+        _p(v_new), int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), _stream(stream)),
+        "paged_kv_prefill")

@@ -216,6 +216,47 @@ int paged_kv_append(const paged_kv_pool* pool, const int32_t* block_table, int64
     return hip_status(pkv::launch_append(p, static_cast<hipStream_t>(stream)));
 }
 
+int paged_kv_prefill(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* start_pos, const int32_t* cu_tokens, int32_t num_seqs,
+                     int32_t total_tokens, uint16_t* q, int64_t q_stride, const uint16_t* k_new,
+                     int64_t k_stride, const uint16_t* v_new, int64_t v_stride,
+                     const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                     void* stream) {
+    if (num_seqs < 0 || total_tokens < 0 || total_tokens > (1 << 30)) return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0 || total_tokens == 0) return PKV_OK;
+    if (!start_pos || !cu_tokens) return PKV_ERR_INVALID_ARG;
+    // q is optional here: with NULL only K/V are written.  Its stride is
+    // checked only when it is given.
+    static const uint16_t kNoQ[8] __attribute__((aligned(16))) = {};
+    const int st = check_append(pool, block_table, bt_stride, start_pos, q ? q : kNoQ,
+                                q ? q_stride : pkv::kQHeads * pkv::kHeadDim, k_new, k_stride,
+                                v_new, v_stride, rope_cos, rope_sin, max_pos);
+    if (st != PKV_OK) return st;
+    pkv::PrefillParams p;
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.num_pages = pool->num_pages;
+    p.page_stride = pool->page_stride;
+    p.head_stride = pool->head_stride;
+    p.slot_stride = pool->slot_stride;
+    p.block_table = block_table;
+    p.bt_stride = bt_stride;
+    p.start_pos = start_pos;
+    p.cu_tokens = cu_tokens;
+    p.num_seqs = num_seqs;
+    p.total_tokens = total_tokens;
+    p.q = q;
+    p.q_stride = q_stride;
+    p.k_new = k_new;
+    p.k_stride = k_stride;
+    p.v_new = v_new;
+    p.v_stride = v_stride;
+    p.rope_cos = rope_cos;
+    p.rope_sin = rope_sin;
+    p.max_pos = max_pos;
+    return hip_status(pkv::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len) {
     if (!pkv::plan_args_ok(num_seqs, max_context_len)) return 0;
     return pkv::make_plan(num_seqs, max_context_len).splits;

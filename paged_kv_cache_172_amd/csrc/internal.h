@@ -35,6 +35,29 @@ struct AppendParams {
     int32_t max_pos;
 };
 
+// Prefill page fill: packed prompt rows; row t of sequence s (cu_tokens[s] <=
+// t < cu_tokens[s+1]) is the token at position start_pos[s] + t - cu_tokens[s].
+struct PrefillParams {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int64_t num_pages, page_stride, head_stride, slot_stride;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* start_pos;
+    const int32_t* cu_tokens;
+    int32_t num_seqs;
+    int32_t total_tokens;
+    uint16_t* q;  // may be null: K/V only
+    int64_t q_stride;
+    const uint16_t* k_new;
+    int64_t k_stride;
+    const uint16_t* v_new;
+    int64_t v_stride;
+    const float* rope_cos;
+    const float* rope_sin;
+    int32_t max_pos;
+};
+
 // The split plan: S outer chunks per (sequence, KV head), each one workgroup
 // of kChunkWaves waves; a sequence of np pages is cut into kChunkWaves * S
 // chunks of ceil(np / (kChunkWaves * S)) pages.
@@ -77,6 +100,7 @@ Plan make_plan(int32_t num_seqs, int32_t max_context_len);
 size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len);
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);

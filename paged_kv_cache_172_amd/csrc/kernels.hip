@@ -160,20 +160,52 @@ __device__ __forceinline__ void rope4(uint2& x1, uint2& x2, float4 c, float4 sn)
     x2 = make_uint2(yb[0], yb[1]);
 }
 
-// Three 128-thread blocks per sequence; a task is 4 rotation pairs of one head
-// (or 16 bytes of V):
+// Three 128-thread blocks per appended token; a task is 4 rotation pairs of
+// one head (or 16 bytes of V):
 //   blocks 0, 1: q tasks 0..255 (head task/8, pairs (task%8)*4 .. +3)
 //   block 2:     threads 0..63 k tasks (head t/8), threads 64..127 copy V.
-// The new-token rows are loaded before the length is known (they do not
-// depend on it); the table row and the page index follow from the length.
+// A prefill without q runs only block 2 of each token.
+// The new-token rows are loaded before the position is known (they do not
+// depend on it); the table row and the page index follow from the position.
 constexpr int kAppendThreads = 128;
-constexpr int kAppendBlocksPerSeq = 3;
+constexpr int kAppendBlocksPerToken = 3;
 
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) {
-    const int s = blockIdx.x / kAppendBlocksPerSeq;
-    const int part = blockIdx.x % kAppendBlocksPerSeq;
+// Where one appended token comes from and goes to.
+struct TokenSite {
+    int seq;   // sequence (block-table row)
+    int row;   // row of q / k / v
+    int pos;   // absolute position; < 0: nothing to do
+};
+
+// Decode: sequence s appends its token at position context_lens[s] - 1.
+__device__ __forceinline__ TokenSite decode_site(const AppendParams& p, int token) {
+    return TokenSite{token, token, p.context_lens[token] - 1};
+}
+
+// Prefill: packed row t belongs to the sequence s with cu_tokens[s] <= t <
+// cu_tokens[s+1] (binary search over the num_seqs + 1 offsets) and sits at
+// position start_pos[s] + t - cu_tokens[s].
+__device__ __forceinline__ TokenSite prefill_site(const PrefillParams& p, int token) {
+    int lo = 0, hi = p.num_seqs;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_tokens[mid + 1] <= token) lo = mid + 1;
+        else hi = mid;
+    }
+    if (lo >= p.num_seqs || token < p.cu_tokens[lo]) return TokenSite{0, token, -1};
+    return TokenSite{lo, token, p.start_pos[lo] + (token - p.cu_tokens[lo])};
+}
+
+template <bool kPrefill, typename Params>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(Params p) {
+    const int parts = p.q ? kAppendBlocksPerToken : 1;
+    const int token = (int)(blockIdx.x / (unsigned)parts);
+    const int part = p.q ? (int)(blockIdx.x % (unsigned)parts) : 2;
     const int tid = threadIdx.x;
     const bool is_v = part == 2 && tid >= 64;
+    TokenSite site;
+    if constexpr (kPrefill) site = prefill_site(p, token);
+    else site = decode_site(p, token);
     // head-vector base and pair offset of this thread's task
     int head, i0;
     const uint16_t* src;
@@ -181,15 +213,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
         const int task = part * kAppendThreads + tid;
         head = task >> 3;
         i0 = (task & 7) * 4;
-        src = p.q + (int64_t)s * p.q_stride + head * kHeadDim;
+        src = p.q + (int64_t)site.row * p.q_stride + head * kHeadDim;
     } else if (!is_v) {
         head = tid >> 3;
         i0 = (tid & 7) * 4;
-        src = p.k_new + (int64_t)s * p.k_stride + head * kHeadDim;
+        src = p.k_new + (int64_t)site.row * p.k_stride + head * kHeadDim;
     } else {
         head = (tid - 64) >> 3;
         i0 = ((tid - 64) & 7) * 8;
-        src = p.v_new + (int64_t)s * p.v_stride + head * kHeadDim;
+        src = p.v_new + (int64_t)site.row * p.v_stride + head * kHeadDim;
     }
     uint2 x1 = make_uint2(0, 0), x2 = make_uint2(0, 0);
     uint4 vrow = make_uint4(0, 0, 0, 0);
@@ -199,16 +231,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendParams p) 
         x1 = *reinterpret_cast<const uint2*>(src + i0);
         x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
     }
-    const int n = p.context_lens[s];
-    if (n < 1) return;
-    const int pos = n - 1;
+    const int pos = site.pos;
+    if (pos < 0) return;
     if (pos >= p.max_pos) return;                 // outside the RoPE table: not dereferenced
     int64_t page = -1;
     const int slot = pos & 15;
     if (part == 2) {
         const int64_t j = pos >> 4;
         if (j >= p.bt_stride) return;
-        page = p.block_table[(int64_t)s * p.bt_stride + j];
+        page = p.block_table[(int64_t)site.seq * p.bt_stride + j];
         if (page < 0 || page >= p.num_pages) return;   // never write through a bad entry
     }
     if (is_v) {
@@ -742,7 +773,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)p.num_seqs * kAppendBlocksPerSeq),
+    hipLaunchKernelGGL((append_kernel<false, AppendParams>),
+                       dim3((unsigned)p.num_seqs * kAppendBlocksPerToken), dim3(kAppendThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+    const int64_t blocks = (int64_t)p.total_tokens * (p.q ? kAppendBlocksPerToken : 1);
+    hipLaunchKernelGGL((append_kernel<true, PrefillParams>), dim3((unsigned)blocks),
                        dim3(kAppendThreads), 0, stream, p);
     return hipGetLastError();
 }

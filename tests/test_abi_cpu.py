@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -230,6 +230,38 @@ def test_fused_rejects(lib, kw, want):
     a.update(kw)
     try:
         pkv.paged_kv_append_decode_attn(_pool(), **a)
+        got = pkv.PKV_OK
+    except pkv.PagedKVError as e:
+        got = e.status
+    assert got == want
+
+
+PREFILL_CASES = [
+    ({"num_seqs": -1}, pkv.PKV_ERR_INVALID_ARG),
+    ({"total_tokens": -1}, pkv.PKV_ERR_INVALID_ARG),
+    ({"total_tokens": (1 << 30) + 1}, pkv.PKV_ERR_INVALID_ARG),
+    ({"start_pos": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"cu_tokens": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"k_new": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"block_table": None}, pkv.PKV_ERR_INVALID_ARG),
+    ({"max_pos": 0}, pkv.PKV_ERR_INVALID_ARG),
+    ({"q_stride": 1024}, pkv.PKV_ERR_INVALID_ARG),
+    ({"q": None, "k_stride": 256}, pkv.PKV_ERR_INVALID_ARG),
+    ({"q": FAKE + 2}, pkv.PKV_ERR_ALIGNMENT),
+    ({"q": None, "v_new": FAKE + 8}, pkv.PKV_ERR_ALIGNMENT),
+    ({"num_seqs": 0}, pkv.PKV_OK),
+    ({"total_tokens": 0}, pkv.PKV_OK),
+]
+
+
+@pytest.mark.parametrize("kw,want", PREFILL_CASES)
+def test_prefill_rejects(lib, kw, want):
+    a = dict(block_table=FAKE, bt_stride=128, start_pos=FAKE, cu_tokens=FAKE, num_seqs=4,
+             total_tokens=100, q=FAKE, q_stride=Q_ROW, k_new=FAKE, k_stride=KV_ROW, v_new=FAKE,
+             v_stride=KV_ROW, rope_cos=FAKE, rope_sin=FAKE, max_pos=2048)
+    a.update(kw)
+    try:
+        pkv.paged_kv_prefill(_pool(), **a)
         got = pkv.PKV_OK
     except pkv.PagedKVError as e:
         got = e.status
