@@ -3,15 +3,19 @@
 The product is ``libpagedkv.so`` (HIP kernels for gfx950 behind the C ABI in
 ``include/paged_kv.h``).  This package holds its sources (``csrc/``), the
 build step (``build.py``), the thin ctypes binding (``_lib.py``, re-exported
-here), the host page allocator for the lazy page step (``pages.py``), and the
+here), the bindings of the native host page management (``pages.py``), and the
 seeded synthetic workload generator (``workload.py``).
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     PKV_ERR_ALIGNMENT,
+    PKV_ERR_BUDGET,
+    PKV_ERR_EXHAUSTED,
     PKV_ERR_HIP,
     PKV_ERR_INVALID_ARG,
+    PKV_ERR_REJECTED,
+    PKV_ERR_STATE,
     PKV_ERR_UNSUPPORTED,
     PKV_ERR_WORKSPACE,
     PKV_OK,

@@ -19,6 +19,10 @@ PKV_ERR_ALIGNMENT = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_UNSUPPORTED = -4
 PKV_ERR_HIP = -5
+PKV_ERR_EXHAUSTED = -6
+PKV_ERR_REJECTED = -7
+PKV_ERR_BUDGET = -8
+PKV_ERR_STATE = -9
 
 EXPORTED = (
     "paged_kv_rope_table",
@@ -31,7 +35,46 @@ EXPORTED = (
     "paged_kv_append_decode_attn",
     "paged_kv_prefill",
     "paged_kv_status_string",
+    # host page management (include/paged_kv_pager.h)
+    "paged_kv_free_list_create",
+    "paged_kv_free_list_destroy",
+    "paged_kv_free_list_pop",
+    "paged_kv_free_list_push",
+    "paged_kv_free_list_stats",
+    "paged_kv_lazy_page_step",
+    "paged_kv_pager_create",
+    "paged_kv_pager_destroy",
+    "paged_kv_pager_submit",
+    "paged_kv_pager_admit",
+    "paged_kv_pager_reserve",
+    "paged_kv_pager_decode_step",
+    "paged_kv_pager_share_prefix",
+    "paged_kv_pager_finish",
+    "paged_kv_pager_get_stats",
 )
+
+
+class PagerStats(ctypes.Structure):
+    """paged_kv_pager_stats."""
+    _fields_ = [
+        ("pool_pages", ctypes.c_int64),
+        ("free_pages", ctypes.c_int64),
+        ("live_pages", ctypes.c_int64),
+        ("peak_live_pages", ctypes.c_int64),
+        ("credit_pages", ctypes.c_int64),
+        ("shared_refs", ctypes.c_int64),
+        ("copies", ctypes.c_int64),
+        ("active_requests", ctypes.c_int32),
+        ("peak_active_requests", ctypes.c_int32),
+        ("waiting_requests", ctypes.c_int32),
+        ("largest_decode_batch", ctypes.c_int32),
+        ("submitted", ctypes.c_int64),
+        ("admitted", ctypes.c_int64),
+        ("rejected", ctypes.c_int64),
+        ("finished", ctypes.c_int64),
+        ("wait_max_us", ctypes.c_double),
+        ("wait_total_us", ctypes.c_double),
+    ]
 
 
 class PagedKVError(RuntimeError):
@@ -83,6 +126,26 @@ def load(path: str = LIB_PATH):
         "paged_kv_prefill": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P, P, i32, P],
                              ctypes.c_int),
         "paged_kv_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "paged_kv_free_list_create": ([P, i64, i64, ctypes.POINTER(P)], ctypes.c_int),
+        "paged_kv_free_list_destroy": ([P], None),
+        "paged_kv_free_list_pop": ([P, ctypes.POINTER(i32)], ctypes.c_int),
+        "paged_kv_free_list_push": ([P, i32], ctypes.c_int),
+        "paged_kv_free_list_stats": ([P, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                      ctypes.POINTER(i64)], ctypes.c_int),
+        "paged_kv_lazy_page_step": ([P, P, i32, i32, i64, P, P, ctypes.POINTER(i32)],
+                                    ctypes.c_int),
+        "paged_kv_pager_create": ([i32, i32, i32, ctypes.POINTER(P)], ctypes.c_int),
+        "paged_kv_pager_destroy": ([P], None),
+        "paged_kv_pager_submit": ([P, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i32)],
+                                  ctypes.c_int),
+        "paged_kv_pager_admit": ([P, P, i32, ctypes.POINTER(i32)], ctypes.c_int),
+        "paged_kv_pager_reserve": ([P, i64, i32, P, i64, P, P, ctypes.POINTER(i32)],
+                                   ctypes.c_int),
+        "paged_kv_pager_decode_step": ([P, P, P, i32, P, i64, i64, P, P, ctypes.POINTER(i32)],
+                                       ctypes.c_int),
+        "paged_kv_pager_share_prefix": ([P, i64, i64, i32, P, i64], ctypes.c_int),
+        "paged_kv_pager_finish": ([P, i64], ctypes.c_int),
+        "paged_kv_pager_get_stats": ([P, ctypes.POINTER(PagerStats)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

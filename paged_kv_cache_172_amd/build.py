@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp"),
+           os.path.join(CSRC, "pager.cpp")]
 ARCH = "gfx950"
 
 

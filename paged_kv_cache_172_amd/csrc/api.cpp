@@ -10,6 +10,7 @@
 
 #include "internal.h"
 #include "paged_kv.h"
+#include "paged_kv_pager.h"
 
 namespace pkv {
 
@@ -359,6 +360,11 @@ const char* paged_kv_status_string(int status) {
         case PKV_ERR_WORKSPACE: return "workspace smaller than paged_decode_attn_workspace_size()";
         case PKV_ERR_UNSUPPORTED: return "unsupported geometry";
         case PKV_ERR_HIP: return g_status_text[0] ? g_status_text : "HIP error";
+        case PKV_ERR_EXHAUSTED: return "KV page pool exhausted: no free page left";
+        case PKV_ERR_REJECTED:
+            return "request rejected: its page budget exceeds the whole KV page pool";
+        case PKV_ERR_BUDGET: return "length beyond the request's admitted budget";
+        case PKV_ERR_STATE: return "unknown request, or request in the wrong state";
         default: return "unknown status";
     }
 }
