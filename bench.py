@@ -121,6 +121,60 @@ def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
     }
 
 
+def time_prefix_sharing(torch, pkv, stream, reps: int):
+    """64 sequences of 2,048 tokens whose first 1,024 tokens are one shared
+    prompt, tables built by the native pager (one layer): live pages with and
+    without sharing, and the attention over the shared layout."""
+    import numpy as np
+    from paged_kv_cache_172_amd import pages as pg
+    from paged_kv_cache_172_amd.runner import HALF_PAGE, PAGE_ELEMS
+    dev = torch.device("cuda", 0)
+    B, n, shared = 64, 2048, 1024
+    pool_pages = B * n // 16          # credits: admission does not count on sharing
+    pager = pg.Pager(pool_pages, 1)
+    ids = [pager.submit(n, 1)[0] for _ in range(B)]
+    assert pager.admit() == ids
+    tables = np.full((B, 1, 128), -1, np.int32)
+    pager.reserve(ids[0], shared, tables[0])
+    for i in range(1, B):
+        pager.share_prefix(ids[0], ids[i], shared, tables[i])
+    assert pager.decode_step(ids, [n] * B, tables) == []
+    st = pager.stats()
+    g = torch.Generator(device=dev).manual_seed(172200)
+    pool_t = torch.randn((pool_pages, 2, 8, 16, 64), generator=g, device=dev).to(torch.bfloat16)
+    pool_t = pool_t.view(torch.int16)
+    base = pool_t.data_ptr()
+    pool = pkv.make_pool(base, base + HALF_PAGE * 2, pool_pages, PAGE_ELEMS, 1024, 64)
+    bt = torch.from_numpy(np.ascontiguousarray(tables[:, 0])).to(dev)
+    ctx = torch.full((B,), n, dtype=torch.int32, device=dev)
+    q = torch.randn((B, 2048), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    out = torch.empty((B, 2048), dtype=torch.float32, device=dev)
+
+    def launch():
+        pkv.paged_decode_attn_split(pool, bt, 128, ctx, B, n, q, 2048, 0.125, out, 2048, None, 0,
+                                    stream)
+
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    logical = B * n * 2048
+    return {
+        "workload": f"{B} sequences x {n} tokens, the first {shared} shared, one layer",
+        "live_pages_shared": st["live_pages"],
+        "live_pages_unshared": B * n // 16,
+        "shared_refs": st["shared_refs"],
+        "attn_us": round(us, 2),
+        "logical_kv_gbps": round(logical / (us * 1e-6) / 1e9, 1),
+        "hbm_kv_bytes": st["live_pages"] * 16 * 2048,
+    }
+
+
 def kernel_source_sha() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -284,6 +338,7 @@ def main():
     split_avg = timed(lambda: [batch.attn_split(layer, stream) for layer in range(L)], a.steps) / L
 
     prefill = time_prefill(torch, pkv, stream, batch.rope_cos, batch.rope_sin, max(3, a.steps // 2))
+    prefix = time_prefix_sharing(torch, pkv, stream, max(3, a.steps))
 
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
@@ -344,6 +399,7 @@ def main():
         },
     }
     result["prefill_fill"] = prefill
+    result["prefix_sharing"] = prefix
     if free_stats:
         result["free_list"] = free_stats
     if not a.no_cpu_baseline:

@@ -163,6 +163,23 @@ int paged_kv_prefill(const paged_kv_pool* pool, const int32_t* block_table, int6
                      void* stream);
 
 /*
+ * Whole-page copies: page dst[i] receives all of page src[i] (K and V, every
+ * KV head, slot and dim), for i < num_pairs, in one launch.  This is the
+ * device half of copy-on-write for pages shared between sequences that
+ * start with the same prompt ("【ITニュース解説】From a Rust Inference Engine
+ * to Heterogeneous Serving", the paragraph on the prefix cache): the host
+ * pager (paged_kv_pager.h) hands out the pairs, and they are copied before
+ * the next token is written.  Pairs naming a page outside [0, num_pages) are
+ * skipped.
+ *   src, dst  (device) int32 [num_pairs]
+ * Preconditions (unchecked): no dst is another pair's src or dst.
+ * Errors: INVALID_ARG (null pointer, num_pairs < 0), ALIGNMENT, HIP.
+ * num_pairs == 0: no-op.
+ */
+int paged_kv_copy_pages(const paged_kv_pool* pool, const int32_t* src, const int32_t* dst,
+                        int32_t num_pairs, void* stream);
+
+/*
  * Split plan of the decode attention.  Each (sequence, KV head) is served by
  * S workgroups of 4 wavefronts.  A sequence whose context fills np pages is
  * cut into 4*S chunks of ceil(np / (4*S)) whole pages, in logical order; each

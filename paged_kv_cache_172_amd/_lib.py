@@ -34,6 +34,7 @@ EXPORTED = (
     "paged_decode_attn_combine",
     "paged_kv_append_decode_attn",
     "paged_kv_prefill",
+    "paged_kv_copy_pages",
     "paged_kv_status_string",
     # host page management (include/paged_kv_pager.h)
     "paged_kv_free_list_create",
@@ -125,6 +126,7 @@ def load(path: str = LIB_PATH):
                                          i32, f32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_kv_prefill": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P, P, i32, P],
                              ctypes.c_int),
+        "paged_kv_copy_pages": ([PP, P, P, i32, P], ctypes.c_int),
         "paged_kv_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "paged_kv_free_list_create": ([P, i64, i64, ctypes.POINTER(P)], ctypes.c_int),
         "paged_kv_free_list_destroy": ([P], None),
@@ -268,3 +270,8 @@ def paged_kv_prefill(pool: Pool, block_table, bt_stride, start_pos, cu_tokens, n
         int(num_seqs), int(total_tokens), _p(q), int(q_stride), _p(k_new), int(k_stride),
         _p(v_new), int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), _stream(stream)),
         "paged_kv_prefill")
+
+
+def paged_kv_copy_pages(pool: Pool, src, dst, num_pairs, stream=None) -> None:
+    _check(load().paged_kv_copy_pages(ctypes.byref(pool), _p(src), _p(dst), int(num_pairs),
+                                      _stream(stream)), "paged_kv_copy_pages")

@@ -258,6 +258,26 @@ int paged_kv_prefill(const paged_kv_pool* pool, const int32_t* block_table, int6
     return hip_status(pkv::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 
+int paged_kv_copy_pages(const paged_kv_pool* pool, const int32_t* src, const int32_t* dst,
+                        int32_t num_pairs, void* stream) {
+    if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
+    if (num_pairs == 0) return PKV_OK;
+    const int st = check_pool(pool);
+    if (st != PKV_OK) return st;
+    if (!src || !dst) return PKV_ERR_INVALID_ARG;
+    pkv::CopyParams p;
+    p.k_pool = pool->k_pool;
+    p.v_pool = pool->v_pool;
+    p.num_pages = pool->num_pages;
+    p.page_stride = pool->page_stride;
+    p.head_stride = pool->head_stride;
+    p.slot_stride = pool->slot_stride;
+    p.src = src;
+    p.dst = dst;
+    p.n = num_pairs;
+    return hip_status(pkv::launch_copy_pages(p, static_cast<hipStream_t>(stream)));
+}
+
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len) {
     if (!pkv::plan_args_ok(num_seqs, max_context_len)) return 0;
     return pkv::make_plan(num_seqs, max_context_len).splits;

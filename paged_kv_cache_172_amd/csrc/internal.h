@@ -58,6 +58,16 @@ struct PrefillParams {
     int32_t max_pos;
 };
 
+// Whole-page copies (copy-on-write of shared prefix pages).
+struct CopyParams {
+    uint16_t* k_pool;
+    uint16_t* v_pool;
+    int64_t num_pages, page_stride, head_stride, slot_stride;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t n;
+};
+
 // The split plan: S outer chunks per (sequence, KV head), each one workgroup
 // of kChunkWaves waves; a sequence of np pages is cut into kChunkWaves * S
 // chunks of ceil(np / (kChunkWaves * S)) pages.
@@ -101,6 +111,7 @@ size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len);
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_copy_pages(const CopyParams& p, hipStream_t stream);
 hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);

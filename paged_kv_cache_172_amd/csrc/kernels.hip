@@ -257,6 +257,34 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Params p) {
     *reinterpret_cast<uint2*>(dst + i0 + 32) = x2;
 }
 
+// --------------------------------------------------------- page copy --
+//
+// Copy-on-write of shared prefix pages: block i copies all of page src[i]
+// (K and V, every head, slot and dim, through the pool strides) to page
+// dst[i], 16 bytes per thread-step.  Pairs with an id outside the pool are
+// skipped.
+constexpr int kCopyThreads = 256;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(CopyParams p) {
+    const int i = blockIdx.x;
+    const int64_t src = p.src[i];
+    const int64_t dst = p.dst[i];
+    if (src < 0 || src >= p.num_pages || dst < 0 || dst >= p.num_pages) return;
+    // 8 heads x 16 slots x 8 chunks of 8 BF16, for K then V
+    constexpr int kChunks = kKVHeads * kPageTokens * (kHeadDim / 8);
+    for (int c = threadIdx.x; c < 2 * kChunks; c += kCopyThreads) {
+        const int half = c / kChunks;
+        const int r = c % kChunks;
+        const int g = r / (kPageTokens * 8);
+        const int t = (r / 8) % kPageTokens;
+        const int d = (r % 8) * 8;
+        const int64_t off = g * p.head_stride + t * p.slot_stride + d;
+        uint16_t* base = half ? p.v_pool : p.k_pool;
+        *reinterpret_cast<uint4*>(base + dst * p.page_stride + off) =
+            *reinterpret_cast<const uint4*>(base + src * p.page_stride + off);
+    }
+}
+
 // ---------------------------------------------------------- attention --
 //
 // One workgroup of 4 wavefronts per (sequence s, KV head g, outer chunk ci);
@@ -776,6 +804,11 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<false, AppendParams>),
                        dim3((unsigned)p.num_seqs * kAppendBlocksPerToken), dim3(kAppendThreads), 0,
                        stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_pages(const CopyParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_pages_kernel, dim3((unsigned)p.n), dim3(kCopyThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -270,3 +270,22 @@ def test_prefill_rejects(lib, kw, want):
     except pkv.PagedKVError as e:
         got = e.status
     assert got == want
+
+
+def test_copy_pages_rejects(lib):
+    def st(**kw):
+        a = dict(src=FAKE, dst=FAKE, num_pairs=3)
+        a.update(kw)
+        try:
+            pkv.paged_kv_copy_pages(_pool(), **a)
+        except pkv.PagedKVError as e:
+            return e.status
+        return pkv.PKV_OK
+    assert st(num_pairs=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert st(src=None) == pkv.PKV_ERR_INVALID_ARG
+    assert st(num_pairs=0, src=None) == pkv.PKV_OK
+    try:
+        pkv.paged_kv_copy_pages(_pool(v_pool=FAKE + 6), FAKE, FAKE, 2)
+        raise AssertionError("misaligned pool accepted")
+    except pkv.PagedKVError as e:
+        assert e.status == pkv.PKV_ERR_ALIGNMENT
