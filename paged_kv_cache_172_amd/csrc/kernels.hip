@@ -160,17 +160,24 @@ __device__ __forceinline__ void rope4(uint2& x1, uint2& x2, float4 c, float4 sn)
     x2 = make_uint2(yb[0], yb[1]);
 }
 
-// Three 128-thread blocks per appended token; a task is 4 rotation pairs of
-// one head (or 16 bytes of V):
+// Three 128-thread blocks per group of appended rows; a task is 4 rotation
+// pairs of one head (or 16 bytes of V), the same task for every row of the
+// group:
 //   blocks 0, 1: q tasks 0..255 (head task/8, pairs (task%8)*4 .. +3)
 //   block 2:     threads 0..63 k tasks (head t/8), threads 64..127 copy V.
-// A prefill without q runs only block 2 of each token.
-// The new-token rows are loaded before the position is known (they do not
-// depend on it); the table row and the page index follow from the position.
+// A prefill without q runs only block 2 of each group.  A block takes kRows
+// consecutive rows: it finds their sequences and positions once (one
+// binary search, then a walk), requests the inputs of all of them, and then
+// rotates and stores row by row, so the latency of those lookups and loads
+// is paid once per group.
 constexpr int kAppendThreads = 128;
 constexpr int kAppendBlocksPerToken = 3;
+#ifndef PKV_PREFILL_ROWS
+#define PKV_PREFILL_ROWS 2
+#endif
+constexpr int kPrefillRows = PKV_PREFILL_ROWS;
 
-// Where one appended token comes from and goes to.
+// Where one appended row comes from and goes to.
 struct TokenSite {
     int seq;   // sequence (block-table row)
     int row;   // row of q / k / v
@@ -178,83 +185,120 @@ struct TokenSite {
 };
 
 // Decode: sequence s appends its token at position context_lens[s] - 1.
-__device__ __forceinline__ TokenSite decode_site(const AppendParams& p, int token) {
-    return TokenSite{token, token, p.context_lens[token] - 1};
+template <int kRows>
+__device__ __forceinline__ void find_sites(const AppendParams& p, int first, TokenSite (&site)[kRows]) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int t = first + r;
+        site[r] = t < p.num_seqs ? TokenSite{t, t, p.context_lens[t] - 1} : TokenSite{0, 0, -1};
+    }
 }
 
 // Prefill: packed row t belongs to the sequence s with cu_tokens[s] <= t <
-// cu_tokens[s+1] (binary search over the num_seqs + 1 offsets) and sits at
-// position start_pos[s] + t - cu_tokens[s].
-__device__ __forceinline__ TokenSite prefill_site(const PrefillParams& p, int token) {
+// cu_tokens[s+1] and sits at position start_pos[s] + t - cu_tokens[s].  The
+// first row's sequence comes from a binary search over the num_seqs + 1
+// offsets, the next rows' from walking forward (skipping empty sequences).
+template <int kRows>
+__device__ __forceinline__ void find_sites(const PrefillParams& p, int first, TokenSite (&site)[kRows]) {
     int lo = 0, hi = p.num_seqs;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (p.cu_tokens[mid + 1] <= token) lo = mid + 1;
+        if (p.cu_tokens[mid + 1] <= first) lo = mid + 1;
         else hi = mid;
     }
-    if (lo >= p.num_seqs || token < p.cu_tokens[lo]) return TokenSite{0, token, -1};
-    return TokenSite{lo, token, p.start_pos[lo] + (token - p.cu_tokens[lo])};
+    int s = lo;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int t = first + r;
+        while (s < p.num_seqs && p.cu_tokens[s + 1] <= t) ++s;
+        const bool ok = t < p.total_tokens && s < p.num_seqs && p.cu_tokens[s] <= t;
+        site[r] = ok ? TokenSite{s, t, p.start_pos[s] + (t - p.cu_tokens[s])} : TokenSite{0, 0, -1};
+    }
 }
 
-template <bool kPrefill, typename Params>
+template <int kRows, typename Params>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(Params p) {
     const int parts = p.q ? kAppendBlocksPerToken : 1;
-    const int token = (int)(blockIdx.x / (unsigned)parts);
+    const int group = (int)(blockIdx.x / (unsigned)parts);
     const int part = p.q ? (int)(blockIdx.x % (unsigned)parts) : 2;
     const int tid = threadIdx.x;
     const bool is_v = part == 2 && tid >= 64;
-    TokenSite site;
-    if constexpr (kPrefill) site = prefill_site(p, token);
-    else site = decode_site(p, token);
+    TokenSite site[kRows];
+    find_sites<kRows>(p, group * kRows, site);
     // head-vector base and pair offset of this thread's task
     int head, i0;
-    const uint16_t* src;
+    const uint16_t* base;
+    int64_t stride;
     if (part < 2) {
         const int task = part * kAppendThreads + tid;
         head = task >> 3;
         i0 = (task & 7) * 4;
-        src = p.q + (int64_t)site.row * p.q_stride + head * kHeadDim;
+        base = p.q + head * kHeadDim;
+        stride = p.q_stride;
     } else if (!is_v) {
         head = tid >> 3;
         i0 = (tid & 7) * 4;
-        src = p.k_new + (int64_t)site.row * p.k_stride + head * kHeadDim;
+        base = p.k_new + head * kHeadDim;
+        stride = p.k_stride;
     } else {
         head = (tid - 64) >> 3;
         i0 = ((tid - 64) & 7) * 8;
-        src = p.v_new + (int64_t)site.row * p.v_stride + head * kHeadDim;
+        base = p.v_new + head * kHeadDim;
+        stride = p.v_stride;
     }
-    uint2 x1 = make_uint2(0, 0), x2 = make_uint2(0, 0);
-    uint4 vrow = make_uint4(0, 0, 0, 0);
-    if (is_v) {
-        vrow = *reinterpret_cast<const uint4*>(src + i0);
-    } else {
-        x1 = *reinterpret_cast<const uint2*>(src + i0);
-        x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
+    // Requests first: the row inputs, the table rows and the page ids.
+    uint2 x1[kRows], x2[kRows];
+    uint4 vrow[kRows];
+    float4 c[kRows], sn[kRows];
+    int64_t page[kRows];
+    bool go[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int pos = site[r].pos;
+        // outside the RoPE table, or no row: nothing is read or written
+        go[r] = pos >= 0 && pos < p.max_pos;
+        x1[r] = x2[r] = make_uint2(0, 0);
+        vrow[r] = make_uint4(0, 0, 0, 0);
+        c[r] = sn[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        page[r] = -1;
+        if (!go[r]) continue;
+        const uint16_t* src = base + (int64_t)site[r].row * stride;
+        if (is_v) {
+            vrow[r] = *reinterpret_cast<const uint4*>(src + i0);
+        } else {
+            x1[r] = *reinterpret_cast<const uint2*>(src + i0);
+            x2[r] = *reinterpret_cast<const uint2*>(src + i0 + 32);
+            c[r] = *reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * 32 + i0);
+            sn[r] = *reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * 32 + i0);
+        }
+        if (part == 2) {
+            const int64_t j = pos >> 4;
+            if (j < p.bt_stride) page[r] = p.block_table[(int64_t)site[r].seq * p.bt_stride + j];
+        }
     }
-    const int pos = site.pos;
-    if (pos < 0) return;
-    if (pos >= p.max_pos) return;                 // outside the RoPE table: not dereferenced
-    int64_t page = -1;
-    const int slot = pos & 15;
-    if (part == 2) {
-        const int64_t j = pos >> 4;
-        if (j >= p.bt_stride) return;
-        page = p.block_table[(int64_t)site.seq * p.bt_stride + j];
-        if (page < 0 || page >= p.num_pages) return;   // never write through a bad entry
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        if (!go[r]) continue;
+        const int slot = site[r].pos & 15;
+        // never write through a bad entry (q is still rotated)
+        const bool to_page = page[r] >= 0 && page[r] < p.num_pages;
+        const int64_t dst_off = page[r] * p.page_stride + head * p.head_stride + slot * p.slot_stride;
+        if (is_v) {
+            if (to_page) *reinterpret_cast<uint4*>(p.v_pool + dst_off + i0) = vrow[r];
+            continue;
+        }
+        uint2 y1 = x1[r], y2 = x2[r];
+        rope4(y1, y2, c[r], sn[r]);
+        uint16_t* dst;
+        if (part < 2) {
+            dst = const_cast<uint16_t*>(base) + (int64_t)site[r].row * stride;
+        } else {
+            if (!to_page) continue;
+            dst = p.k_pool + dst_off;
+        }
+        *reinterpret_cast<uint2*>(dst + i0) = y1;
+        *reinterpret_cast<uint2*>(dst + i0 + 32) = y2;
     }
-    if (is_v) {
-        uint16_t* dst = p.v_pool + page * p.page_stride + head * p.head_stride + slot * p.slot_stride;
-        *reinterpret_cast<uint4*>(dst + i0) = vrow;
-        return;
-    }
-    const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + (int64_t)pos * 32 + i0);
-    const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + (int64_t)pos * 32 + i0);
-    rope4(x1, x2, c, sn);
-    uint16_t* dst = part < 2
-        ? const_cast<uint16_t*>(src)
-        : p.k_pool + page * p.page_stride + head * p.head_stride + slot * p.slot_stride;
-    *reinterpret_cast<uint2*>(dst + i0) = x1;
-    *reinterpret_cast<uint2*>(dst + i0 + 32) = x2;
 }
 
 // --------------------------------------------------------- page copy --
@@ -801,7 +845,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((append_kernel<false, AppendParams>),
+    hipLaunchKernelGGL((append_kernel<1, AppendParams>),
                        dim3((unsigned)p.num_seqs * kAppendBlocksPerToken), dim3(kAppendThreads), 0,
                        stream, p);
     return hipGetLastError();
@@ -813,8 +857,9 @@ hipError_t launch_copy_pages(const CopyParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-    const int64_t blocks = (int64_t)p.total_tokens * (p.q ? kAppendBlocksPerToken : 1);
-    hipLaunchKernelGGL((append_kernel<true, PrefillParams>), dim3((unsigned)blocks),
+    const int64_t groups = ((int64_t)p.total_tokens + kPrefillRows - 1) / kPrefillRows;
+    const int64_t blocks = groups * (p.q ? kAppendBlocksPerToken : 1);
+    hipLaunchKernelGGL((append_kernel<kPrefillRows, PrefillParams>), dim3((unsigned)blocks),
                        dim3(kAppendThreads), 0, stream, p);
     return hipGetLastError();
 }
