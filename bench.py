@@ -66,12 +66,16 @@ def append_bytes_per_launch(num_seqs: int) -> int:
 PREFILL_SEQS, PREFILL_TOKENS = 64, 2048
 
 
+ROPE_TABLE_BYTES = 2 * 2048 * 32 * 4
+
+
 def prefill_bytes_per_token(with_q: bool) -> int:
     """Algorithmic bytes of the prefill fill per prompt token: k and v rows
-    read (1 KiB each), K' and V rows written into the pages (1 KiB each), the
-    two RoPE table rows (128 B each) and, with q, its row read and written
-    back (4 KiB each)."""
-    return 4 * 1024 + 256 + (8 * 1024 if with_q else 0)
+    read (1 KiB each), K' and V rows written into the pages (1 KiB each) and,
+    with q, its row read and written back (4 KiB each).  The RoPE table is
+    read once per launch (ROPE_TABLE_BYTES): rows are shared by every token
+    at the same position."""
+    return 4 * 1024 + (8 * 1024 if with_q else 0)
 
 
 def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
@@ -108,7 +112,7 @@ def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
-    alg = T * prefill_bytes_per_token(True)
+    alg = T * prefill_bytes_per_token(True) + ROPE_TABLE_BYTES
     gbps = alg / (us * 1e-6) / 1e9
     return {
         "workload": f"{B} prompts x {n} tokens, one layer, q rotated in place",
