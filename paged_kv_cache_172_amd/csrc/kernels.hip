@@ -683,20 +683,6 @@ void attn_split_kernel(AttnParams p) {
             nt.page = np - 1;
             nt.slot = pos & (kPageTokens - 1);
         }
-        if (rotate && ci == 0 && w == 0 && lane < 16) {
-            const int64_t jpage = pos >> 4;
-            if (jpage < p.bt_stride) {
-                const int64_t page = bt_row[jpage];
-                if (page >= 0 && page < p.num_pages) {   // never write through a bad entry
-                    const int64_t dst = page * p.page_stride + g * p.head_stride +
-                                        (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
-                    const int i8 = (lane & 7) * 8;
-                    const uint4 val = *reinterpret_cast<const uint4*>(
-                        &rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
-                    *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
-                }
-            }
-        }
     }
 
     if (pb < pe) {
@@ -810,6 +796,29 @@ void attn_split_kernel(AttnParams p) {
         const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + ci;
         p.ws_acc[slot_idx * kHeadDim + lane] = o;
         if (lane == 0) p.ws_ml[slot_idx] = make_float2(Mx, L);
+    }
+    if constexpr (kFused) {
+        // Fused append, part 3: wave 0 of outer chunk 0 stores the new K/V
+        // row where append_kernel would.  Last, next to the output: a store
+        // counts against the same in-order memory counter as the page loads,
+        // so an early one would hold back this wave's waits for its pages.
+        if (rotate && ci == 0 && w == 0 && lane < 16) {
+            const int64_t jpage = pos >> 4;
+            if (jpage < p.bt_stride) {
+                // From the table registers when the entry is among the first 128.
+                const int64_t page = jpage < bt_w ? (jpage < 64 ? __builtin_amdgcn_readlane(tbl0, (int)jpage)
+                                                                : __builtin_amdgcn_readlane(tbl1, (int)jpage - 64))
+                                                  : bt_row[jpage];
+                if (page >= 0 && page < p.num_pages) {   // never write through a bad entry
+                    const int64_t dst = page * p.page_stride + g * p.head_stride +
+                                        (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
+                    const int i8 = (lane & 7) * 8;
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        &rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
+                    *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
+                }
+            }
+        }
     }
 }
 
