@@ -12,8 +12,10 @@
 //     (attn_split_kernel + attn_combine_kernel).
 // Decode is bound by memory bandwidth ("Tiny-vLLMでゼロから構築する高性能LLM推論
 // エンジン", section "Prefill vs. Decode"), so the attention kernel is shaped
-// around HBM reads: 16-byte loads, a prefetch distance of two pages, and no
-// matrix cores.
+// around HBM reads: 16-byte loads and a prefetch distance of three pages.  The
+// one contraction that suits the matrix cores, Q K^T of the 4 query heads
+// over a page, runs there to take work off the vector ALUs; the softmax and
+// the weighted V sum stay in FP32 on the vector ALUs.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -23,14 +25,9 @@
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ helpers --
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -39,6 +36,10 @@ constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppQuadRev = 0x1B;       // quad_perm [3,2,1,0]: lane ^ 3
+constexpr int kDppRowHalfMirror = 0x141; // lane ^ 7 inside each half row
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -46,34 +47,26 @@ __device__ __forceinline__ float dpp(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum of the four lanes of each quad, on every lane of the quad.
-__device__ __forceinline__ float quad_sum(float x) {
+// Max / sum over the 16 lanes of each row, on every lane of the row.
+__device__ __forceinline__ float row_max(float x) {
+    x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp<kDppRowRor4>(x));
+    return fmaxf(x, dpp<kDppRowRor8>(x));
+}
+__device__ __forceinline__ float row_sum(float x) {
     x += dpp<kDppQuadXor1>(x);
     x += dpp<kDppQuadXor2>(x);
-    return x;
+    x += dpp<kDppRowRor4>(x);
+    return x + dpp<kDppRowRor8>(x);
 }
-
-// Exchange across 32-lane halves / odd-even rows (v_permlane32_swap /
-// v_permlane16_swap).  Returns {new a, new b}.
-struct Pair {
-    float a, b;
-};
-__device__ __forceinline__ Pair swap32(float a, float b) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ Pair swap16(float a, float b) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-// Max over lanes {i, i^4, i^8, ...}: all 16 quads of the wave (lane bits 2..5).
-__device__ __forceinline__ float max_over_quads(float x) {
-    x = fmaxf(x, dpp<kDppRowRor4>(x));
-    x = fmaxf(x, dpp<kDppRowRor8>(x));
-    Pair p = swap16(x, x);
-    x = fmaxf(p.a, p.b);
-    p = swap32(x, x);
-    return fmaxf(p.a, p.b);
+// One step of a reduce-scatter between lane pairs: this lane keeps `a` if
+// `hi` is clear, else `b`, and adds the partner's copy of the one it keeps.
+template <int kCtrl>
+__device__ __forceinline__ float keep_add(float a, float b, bool hi) {
+    const float keep = hi ? b : a;
+    const float send = hi ? a : b;
+    return keep + dpp<kCtrl>(send);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -334,26 +327,28 @@ __global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(CopyParams p) 
 // One workgroup of 4 wavefronts per (sequence s, KV head g, outer chunk ci);
 // it serves the 4 query heads 4g..4g+3.  The sequence's np pages are cut into
 // 4*S chunks of ceil(np / (4*S)) pages and wave w takes chunk 4*ci + w, so the
-// chunk boundaries follow each sequence's own length.  Inside a page the 64
-// lanes are 16 quads: quad t (lanes 4t..4t+3) owns token slot t, and lane
-// quarter c4 = lane%4 owns dims [8*c4, 8*c4+8) and [32+8*c4, 32+8*c4+8) of that
-// token's K and V row (two 16-byte loads each; four consecutive lanes read 64
-// contiguous bytes).
+// chunk boundaries follow each sequence's own length.  Inside a page, lane l
+// owns token slot t = l & 15 and the dims [8*c4, 8*c4+8) and [32+8*c4,
+// 32+8*c4+8), c4 = l >> 4, of that token's K and V row (two 16-byte loads
+// each; the 16 lanes of a row read 16 token rows, 4 rows of lanes cover 64
+// contiguous bytes of each).
 //
-// Per page: QK^T is 8 v_dot2_f32_bf16 per head per lane plus a 2-step DPP
-// quad sum; every quad then runs its own FP32 online softmax over the tokens
-// it owns (slot t of every page of the chunk), with a running maximum that is
-// raised only when a logit exceeds it by more than kRescaleSlack (base-2
-// units; values p = 2^(x - m) stay below 2^kRescaleSlack, so nothing
-// overflows).  At the end of the chunk the 16 quads are merged with the
-// log-sum-exp rule through permlane swaps and DPP, the 4 waves of the
-// workgroup are merged the same way through LDS, and the workgroup writes the
+// Per page: Q K^T is two v_mfma_f32_16x16x32_bf16 (bf16 products are exact in
+// FP32, and the sums are FP32), laid out so that every lane receives the 4
+// heads' logits of its own token.  Each of the 16 token streams (slot t of
+// every page of the chunk; the 4 lane rows hold copies) then runs its own
+// FP32 online softmax, with a running maximum that is raised only when a
+// logit exceeds it by more than kRescaleSlack (base-2 units; values p =
+// 2^(x - m) stay below 2^kRescaleSlack, so nothing overflows), and adds p
+// times its V dims with FP32 FMAs.  At the end of the chunk the 16 streams
+// are merged with the log-sum-exp rule by DPP inside each row, the 4 waves of
+// the workgroup the same way through LDS, and the workgroup writes the
 // normalised output (S = 1) or one partial (max, sum, 64-wide accumulator) per
 // query head for the combine kernel (S > 1).
 
 constexpr float kRescaleSlack = 8.0f;
 #ifndef PKV_RING
-#define PKV_RING 3
+#define PKV_RING 4
 #endif
 constexpr int kRing = PKV_RING;  // page buffers per wave: kRing-1 pages in flight
 static_assert(kRing >= 2 && kRing <= 8, "ring size");
@@ -376,6 +371,7 @@ struct SoftmaxState {
 // into a no-op that returns zeros without touching memory, which is how
 // prefetches past the end of a chunk are issued without branches.
 constexpr int32_t kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
+constexpr int kStoreNonTemporal = 2;          // cache policy bit "nt" of a buffer store
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferWord3);
@@ -418,25 +414,23 @@ struct PageRing {
     }
 };
 
+struct QRegs {
+    bf16x8_t a, b;   // A operands: query head (lane & 3), dims 8c..8c+7 / 32+8c..32+8c+7
+};
+
 template <bool kMasked>
-__device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGroup],
-                                             const uint4 (&qb)[kGroup], float scale_log2,
+__device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float scale_log2,
                                              bool valid, SoftmaxState& st) {
+    // S = Q K^T on the matrix cores: A = the 4 query heads repeated over the
+    // 16 rows, B = this page's K (column = token = lane & 15, k = the lane's 8
+    // dims); row 4(lane>>4)+r of the result is head r, so every lane gets the
+    // 4 heads' logits of its token.
+    f32x4_t acc4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a, __builtin_bit_cast(bf16x8_t, pg.ka), acc4, 0, 0, 0);
+    acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.b, __builtin_bit_cast(bf16x8_t, pg.kb), acc4, 0, 0, 0);
     float x[kGroup];
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-        float s0 = dot2_bf16(qa[r].x, pg.ka.x, 0.0f);
-        float s1 = dot2_bf16(qb[r].x, pg.kb.x, 0.0f);
-        s0 = dot2_bf16(qa[r].y, pg.ka.y, s0);
-        s1 = dot2_bf16(qb[r].y, pg.kb.y, s1);
-        s0 = dot2_bf16(qa[r].z, pg.ka.z, s0);
-        s1 = dot2_bf16(qb[r].z, pg.kb.z, s1);
-        s0 = dot2_bf16(qa[r].w, pg.ka.w, s0);
-        s1 = dot2_bf16(qb[r].w, pg.kb.w, s1);
-        x[r] = s0 + s1;
-    }
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) x[r] = quad_sum(x[r]) * scale_log2;
+    for (int r = 0; r < kGroup; ++r) x[r] = acc4[r] * scale_log2;
     if (kMasked) {
 #pragma unroll
         for (int r = 0; r < kGroup; ++r) x[r] = valid ? x[r] : -INFINITY;
@@ -445,7 +439,7 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGro
     }
     // Largest excess of a new logit over its running maximum (NaN-free: a
     // masked logit is -inf and m is finite or -inf, and -inf - -inf only
-    // occurs for a masked slot whose quad has seen nothing, which excess
+    // occurs for a masked slot whose stream has seen nothing, which excess
     // ignores because fmaxf drops the NaN).
     float excess = x[0] - st.m[0];
 #pragma unroll
@@ -486,14 +480,13 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const uint4 (&qa)[kGro
 // kRing-1 is free.  Step I issues page j+kRing-1 into the slot freed by the
 // previous step, then consumes slot I.
 template <int I, typename Issue>
-__device__ __forceinline__ void ring_round(PageRing& ring, int& j, const uint4 (&qa)[kGroup],
-                                           const uint4 (&qb)[kGroup], float sl2,
+__device__ __forceinline__ void ring_round(PageRing& ring, int& j, const QRegs& q, float sl2,
                                            SoftmaxState& st, Issue& issue) {
     if constexpr (I < kRing) {
         ring.template at<(I + kRing - 1) % kRing>() = issue(j + kRing - 1);
-        consume_page<false>(ring.template at<I>(), qa, qb, sl2, true, st);
+        consume_page<false>(ring.template at<I>(), q, sl2, true, st);
         ++j;
-        ring_round<I + 1>(ring, j, qa, qb, sl2, st, issue);
+        ring_round<I + 1>(ring, j, q, sl2, st, issue);
     }
 }
 
@@ -513,19 +506,19 @@ struct NewToken {
 // sequence's last page and so of a tail; there its slot is masked (what the
 // page held when it was loaded may predate the append), and the wave then
 // consumes the token from LDS in one more masked step.  A masked slot
-// leaves its quad's state bit for bit unchanged, and the token is the last
-// one its quad sees either way, so the result is the one of a separate
+// leaves its stream's state bit for bit unchanged, and the token is the last
+// one its stream sees either way, so the result is the one of a separate
 // append followed by the attention.
 template <int I>
 __device__ __forceinline__ void ring_tail(PageRing& ring, int j, int left, int n, int t,
-                                          const uint4 (&qa)[kGroup], const uint4 (&qb)[kGroup],
-                                          float sl2, const NewToken& nt, SoftmaxState& st) {
+                                          const QRegs& q, float sl2, const NewToken& nt,
+                                          SoftmaxState& st) {
     if constexpr (I < kRing) {
         if (I < left) {
             const bool stale = j + I == nt.page && t == nt.slot;
-            consume_page<true>(ring.template at<I>(), qa, qb, sl2,
+            consume_page<true>(ring.template at<I>(), q, sl2,
                                t < n - (j + I) * kPageTokens && !stale, st);
-            ring_tail<I + 1>(ring, j, left, n, t, qa, qb, sl2, nt, st);
+            ring_tail<I + 1>(ring, j, left, n, t, q, sl2, nt, st);
         }
     }
 }
@@ -569,8 +562,8 @@ void attn_split_kernel(AttnParams p) {
     const uint32_t rest = wg / kKVHeads;
     const int s = (int)(rest % (uint32_t)p.num_seqs);
     const int ci = (int)(rest / (uint32_t)p.num_seqs);
-    const int t = lane >> 2;   // token slot owned by this lane's quad
-    const int c4 = lane & 3;   // dim quarter owned inside the quad
+    const int t = lane & 15;   // token slot of this lane (the MFMA column)
+    const int c4 = lane >> 4;  // dims 8*c4..8*c4+7 and 32+8*c4..32+8*c4+7 (the MFMA k slice)
 
     // Independent loads first: the table row (first 128 entries, one per
     // lane in two registers), q of the 4 query heads, and the length.
@@ -579,14 +572,12 @@ void attn_split_kernel(AttnParams p) {
                                                               : kMaxContext / kPageTokens;
     const int32_t tbl0 = lane < bt_w ? bt_row[lane] : 0;
     const int32_t tbl1 = lane + 64 < bt_w ? bt_row[lane + 64] : 0;
-    uint4 qa[kGroup], qb[kGroup];
+    QRegs q;
     const uint16_t* qrow = p.q + (int64_t)s * p.q_stride + (kGroup * g) * kHeadDim;
     if constexpr (!kFused) {
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-            qa[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + c4 * 8);
-            qb[r] = *reinterpret_cast<const uint4*>(qrow + r * kHeadDim + 32 + c4 * 8);
-        }
+        const uint16_t* qh = qrow + (lane & 3) * kHeadDim + c4 * 8;
+        q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qh));
+        q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qh + 32));
     }
     const int ctx = uniform(p.context_lens[s]);
     const int n = ctx < p.max_context_len ? ctx : p.max_context_len;
@@ -603,10 +594,12 @@ void attn_split_kernel(AttnParams p) {
     // position inside the RoPE table); otherwise q is used as given.
     const int pos = ctx - 1;
     const bool rotate = kFused && ctx >= 1 && pos < p.max_pos;
-    float u[16];          // after the wave merge: row R's head, this lane's 16 dims
+    // After the wave merge: 4 sums of head 2*b3+b2 (b = bits of t), dims
+    // 32*b1 + 8*c4 + 4*b0 .. +3, and that head's (max, sum).
+    f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f};
     float mrow = -INFINITY, lsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) u[k] = 0.0f;
+    const bool b3 = (t & 8) != 0, b2 = (t & 4) != 0, b1 = (t & 2) != 0, b0 = (t & 1) != 0;
+    const int head = (b3 ? 2 : 0) + (b2 ? 1 : 0);
     bool bad_page = false;
 
     const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
@@ -674,11 +667,8 @@ void attn_split_kernel(AttnParams p) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-            qa[r] = *reinterpret_cast<const uint4*>(&rot[r * 32 + c4 * 4]);
-            qb[r] = *reinterpret_cast<const uint4*>(&rot[r * 32 + 16 + c4 * 4]);
-        }
+        q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + c4 * 4]));
+        q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + 16 + c4 * 4]));
         if (rotate && ctx == n) {
             nt.page = np - 1;
             nt.slot = pos & (kPageTokens - 1);
@@ -699,9 +689,9 @@ void attn_split_kernel(AttnParams p) {
 
         int j = pb;
         const int rounds = (pe - 1 - pb) / kRing;   // whole rounds of unmasked pages
-        for (int r = 0; r < rounds; ++r) ring_round<0>(ring, j, qa, qb, sl2, st, issue);
+        for (int r = 0; r < rounds; ++r) ring_round<0>(ring, j, q, sl2, st, issue);
         ring.template at<kRing - 1>() = issue(j + kRing - 1);
-        ring_tail<0>(ring, j, pe - j, n, t, qa, qb, sl2, nt, st);
+        ring_tail<0>(ring, j, pe - j, n, t, q, sl2, nt, st);
         if constexpr (kFused) {
             if (nt.page >= pb && nt.page < pe) {
                 PageRegs pg;
@@ -709,71 +699,45 @@ void attn_split_kernel(AttnParams p) {
                 pg.kb = *reinterpret_cast<const uint4*>(nt.k_row + 16 + c4 * 4);
                 pg.va = *reinterpret_cast<const uint4*>(nt.v_row + c4 * 4);
                 pg.vb = *reinterpret_cast<const uint4*>(nt.v_row + 16 + c4 * 4);
-                consume_page<true>(pg, qa, qb, sl2, t == nt.slot, st);
+                consume_page<true>(pg, q, sl2, t == nt.slot, st);
             }
         }
 
-        // ---- merge the 16 quads of the wave (log-sum-exp rule) ----
-        float M[kGroup];
+        // ---- merge the 16 token streams of each row (log-sum-exp rule) ----
+        float M[kGroup], Ls[kGroup];
 #pragma unroll
-        for (int r = 0; r < kGroup; ++r) M[r] = max_over_quads(st.m[r]);  // finite: slot pb*16 is valid
+        for (int r = 0; r < kGroup; ++r) M[r] = row_max(st.m[r]);  // finite: slot pb*16 is valid
 #pragma unroll
         for (int r = 0; r < kGroup; ++r) {
             const float alpha = st.m[r] == -INFINITY ? 0.0f : exp2_fast(st.m[r] - M[r]);
-            st.l[r] *= alpha;
+            Ls[r] = row_sum(st.l[r] * alpha);
 #pragma unroll
             for (int k = 0; k < 16; ++k) st.acc[r][k] *= alpha;
         }
-        // Sum over lane bit 5 (permlane32 swap): lanes 0..31 keep heads 0/1,
-        // 32..63 heads 2/3; then over lane bit 4 (permlane16 swap): row R
-        // (lanes 16R..16R+15) keeps head R.
-        {
-            float t0[16], t1[16];
+        // Reduce-scatter over the row in 4 pair steps (partners t^8, t^7, t^3,
+        // t^1, which together reach all 16 lanes once): heads by b3 then b2,
+        // then the dim half by b1 and the dim quarter by b0.
+        float v1[2][16], v2[16], v3[8];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                Pair a = swap32(st.acc[0][k], st.acc[2][k]);
-                t0[k] = a.a + a.b;
-                Pair b = swap32(st.acc[1][k], st.acc[3][k]);
-                t1[k] = b.a + b.b;
-            }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                Pair a = swap16(t0[k], t1[k]);
-                u[k] = a.a + a.b;
-            }
-            Pair la = swap32(st.l[0], st.l[2]);
-            Pair lb = swap32(st.l[1], st.l[3]);
-            Pair lc = swap16(la.a + la.b, lb.a + lb.b);
-            lsum = lc.a + lc.b;
-        }
-        // Sum over lane bits 2..3 (the 4 quads of a row) with DPP row rotations.
+            for (int k = 0; k < 16; ++k) v1[h][k] = keep_add<kDppRowRor8>(st.acc[h][k], st.acc[h + 2][k], b3);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            u[k] += dpp<kDppRowRor4>(u[k]);
-            u[k] += dpp<kDppRowRor8>(u[k]);
-        }
-        lsum += dpp<kDppRowRor4>(lsum);
-        lsum += dpp<kDppRowRor8>(lsum);
-        const int row = lane >> 4;
-        mrow = M[0];
-        mrow = row == 1 ? M[1] : mrow;
-        mrow = row == 2 ? M[2] : mrow;
-        mrow = row == 3 ? M[3] : mrow;
+        for (int k = 0; k < 16; ++k) v2[k] = keep_add<kDppRowHalfMirror>(v1[0][k], v1[1][k], b2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v3[k] = keep_add<kDppQuadRev>(v2[k], v2[k + 8], b1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u[k] = keep_add<kDppQuadXor1>(v3[k], v3[k + 4], b0);
+        mrow = head == 0 ? M[0] : head == 1 ? M[1] : head == 2 ? M[2] : M[3];
+        lsum = head == 0 ? Ls[0] : head == 1 ? Ls[1] : head == 2 ? Ls[2] : Ls[3];
         if (bad_page) lsum = NAN;
     }
 
     // ---- merge the 4 chunks of the workgroup through LDS ----
     {
-        const int row = lane >> 4;               // query head 4g + row
-        const int qd = (lane >> 2) & 3;          // which 4 of the lane's 16 values it stores
-        float4 v4;
-        v4.x = qd == 0 ? u[0] : qd == 1 ? u[4] : qd == 2 ? u[8] : u[12];
-        v4.y = qd == 0 ? u[1] : qd == 1 ? u[5] : qd == 2 ? u[9] : u[13];
-        v4.z = qd == 0 ? u[2] : qd == 1 ? u[6] : qd == 2 ? u[10] : u[14];
-        v4.w = qd == 0 ? u[3] : qd == 1 ? u[7] : qd == 2 ? u[11] : u[15];
-        const int dim0 = c4 * 8 + (qd & 1) * 4 + (qd >> 1) * 32;
-        *reinterpret_cast<float4*>(&lds_acc[w][row][dim0]) = v4;
-        if ((lane & 15) == 0) lds_ml[w][row] = make_float2(mrow, lsum);
+        const int dim0 = (b1 ? 32 : 0) + c4 * 8 + (b0 ? 4 : 0);
+        *reinterpret_cast<float4*>(&lds_acc[w][head][dim0]) = make_float4(u[0], u[1], u[2], u[3]);
+        if (c4 == 0 && (t & 3) == 0) lds_ml[w][head] = make_float2(mrow, lsum);
     }
     __syncthreads();
     // Wave w finishes query head 4g + w; lane = output dim.
@@ -791,7 +755,11 @@ void attn_split_kernel(AttnParams p) {
     }
     const int h = kGroup * g + r;
     if (p.plan.splits == 1) {
-        p.out[(int64_t)s * p.out_stride + h * kHeadDim + lane] = L == 0.0f ? 0.0f : o / L;
+        const float ov = L == 0.0f ? 0.0f : o / L;
+        const char* ob = reinterpret_cast<const char*>(p.out + (int64_t)s * p.out_stride + h * kHeadDim);
+        // Non-temporal: nothing in this launch reads the output again.
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), tile_rsrc(ob, kHeadDim * 4), lane * 4, 0,
+                                              kStoreNonTemporal);
     } else {
         const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + ci;
         p.ws_acc[slot_idx * kHeadDim + lane] = o;
