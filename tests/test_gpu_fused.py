@@ -150,3 +150,45 @@ def test_fused_full_size_equals_append_then_attn(torch_gpu, rope, k):
     assert same_bits(torch, fus.q, q_before)
     del sep, fus
     torch.cuda.empty_cache()
+
+
+def test_fused_strided_layouts(torch_gpu, rope):
+    """Packed QKV rows ([B][3072]), padded output rows and a [slot][head][dim]
+    page layout: the fused call gives the bits of append + attention on the
+    default layout, writes the K/V rows through the strides, and leaves the
+    packed q, k and v as given."""
+    torch = torch_gpu
+    spec = wl.make_spec([5, 16, 17, 300, 2048, 64], 1, seed=511)
+    hw = wl.make_host_workload(spec)
+    base = host_batch(hw, rope)
+    base.step()
+    torch.cuda.synchronize()
+    ref_out = base.out[0].clone()
+    ref_pool = base.pool_pages.clone()
+    B = spec.num_seqs
+    dev = base.device
+    # pool with [K|V][slot 16][head 8][dim 64] pages
+    inter = torch.from_numpy(np.ascontiguousarray(hw.pages.transpose(0, 1, 3, 2, 4)).view(np.int16)).to(dev)
+    half = 16 * 8 * 64
+    pool = pkv.make_pool(inter.data_ptr(), inter.data_ptr() + 2 * half, spec.num_pages,
+                         2 * half, 64, 512)
+    qkv = torch.zeros((B, 3072), dtype=torch.int16, device=dev)
+    qkv[:, :2048] = torch.from_numpy(hw.q[0].view(np.int16)).to(dev)
+    qkv[:, 2048:2560] = torch.from_numpy(hw.k[0].view(np.int16)).to(dev)
+    qkv[:, 2560:] = torch.from_numpy(hw.v[0].view(np.int16)).to(dev)
+    qkv_before = qkv.clone()
+    bt = torch.from_numpy(np.ascontiguousarray(spec.block_tables[0])).to(dev)
+    ctx = torch.from_numpy(spec.ctx).to(dev)
+    out = torch.zeros((B, 2056), dtype=torch.float32, device=dev)   # padded rows
+    ws_bytes = pkv.paged_decode_attn_workspace_size(B, base.max_context_len)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    say(f"fused strided layouts: B={B} ctx={spec.ctx.tolist()}")
+    pkv.paged_kv_append_decode_attn(pool, bt, 128, ctx, B, base.max_context_len, qkv, 3072,
+                                    qkv[:, 2048:], 3072, qkv[:, 2560:], 3072, base.rope_cos,
+                                    base.rope_sin, 2048, base.scale, out, 2056, ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert same_bits(torch, out[:, :2048].contiguous(), ref_out), "output differs from append + attention"
+    assert torch.equal(out[:, 2048:], torch.zeros_like(out[:, 2048:])), "padding written"
+    back = inter.view(spec.num_pages, 2, 16, 8, 64).permute(0, 1, 3, 2, 4).contiguous()
+    assert torch.equal(back, ref_pool.view(back.shape)), "pool differs from append"
+    assert torch.equal(qkv, qkv_before), "the fused call must leave q, k and v as given"
