@@ -12,10 +12,11 @@
 //     (attn_split_kernel + attn_combine_kernel).
 // Decode is bound by memory bandwidth ("Tiny-vLLMでゼロから構築する高性能LLM推論
 // エンジン", section "Prefill vs. Decode"), so the attention kernel is shaped
-// around HBM reads: 16-byte loads and a prefetch distance of three pages.  The
-// one contraction that suits the matrix cores, Q K^T of the 4 query heads
-// over a page, runs there to take work off the vector ALUs; the softmax and
-// the weighted V sum stay in FP32 on the vector ALUs.
+// around HBM reads: 16-byte loads and a prefetch distance of two pages.  The
+// two contractions of a page, Q K^T of the 4 query heads and the weighted
+// sum of V over its 16 tokens, run on the matrix cores to take work off the
+// vector ALUs; the softmax is FP32, its weights enter the V product as two
+// BF16 terms each, and every sum is FP32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -32,13 +33,15 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // DPP lane movement inside 16-lane rows.
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
-constexpr int kDppQuadRev = 0x1B;       // quad_perm [3,2,1,0]: lane ^ 3
-constexpr int kDppRowHalfMirror = 0x141; // lane ^ 7 inside each half row
+constexpr int kDppQuadBcast0 = 0x00;  // quad_perm [0,0,0,0]: lane 0 of each quad to all 4
+constexpr int kDppQuadBcast1 = 0x55;  // quad_perm [1,1,1,1]
+constexpr int kDppQuadBcast2 = 0xAA;  // quad_perm [2,2,2,2]
+constexpr int kDppQuadBcast3 = 0xFF;  // quad_perm [3,3,3,3]
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int kCtrl>
@@ -47,26 +50,19 @@ __device__ __forceinline__ float dpp(float x) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
 }
 
-// Max / sum over the 16 lanes of each row, on every lane of the row.
-__device__ __forceinline__ float row_max(float x) {
-    x = fmaxf(x, dpp<kDppQuadXor1>(x));
-    x = fmaxf(x, dpp<kDppQuadXor2>(x));
-    x = fmaxf(x, dpp<kDppRowRor4>(x));
-    return fmaxf(x, dpp<kDppRowRor8>(x));
+// Max / sum across the 4 rows of 16 lanes (lane bits 4 and 5), with
+// v_permlane16_swap and v_permlane32_swap.
+__device__ __forceinline__ float cross_rows_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float row_sum(float x) {
-    x += dpp<kDppQuadXor1>(x);
-    x += dpp<kDppQuadXor2>(x);
-    x += dpp<kDppRowRor4>(x);
-    return x + dpp<kDppRowRor8>(x);
-}
-// One step of a reduce-scatter between lane pairs: this lane keeps `a` if
-// `hi` is clear, else `b`, and adds the partner's copy of the one it keeps.
-template <int kCtrl>
-__device__ __forceinline__ float keep_add(float a, float b, bool hi) {
-    const float keep = hi ? b : a;
-    const float send = hi ? a : b;
-    return keep + dpp<kCtrl>(send);
+__device__ __forceinline__ float cross_rows_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -328,27 +324,28 @@ __global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(CopyParams p) 
 // it serves the 4 query heads 4g..4g+3.  The sequence's np pages are cut into
 // 4*S chunks of ceil(np / (4*S)) pages and wave w takes chunk 4*ci + w, so the
 // chunk boundaries follow each sequence's own length.  Inside a page, lane l
-// owns token slot t = l & 15 and the dims [8*c4, 8*c4+8) and [32+8*c4,
-// 32+8*c4+8), c4 = l >> 4, of that token's K and V row (two 16-byte loads
-// each; the 16 lanes of a row read 16 token rows, 4 rows of lanes cover 64
-// contiguous bytes of each).
+// loads the dims [8*c4, 8*c4+8) and [32+8*c4, 32+8*c4+8), c4 = l >> 4, of
+// token slot l & 15's K and V row (two 16-byte loads each; the 16 lanes of a
+// row read 16 token rows, 4 rows of lanes cover 64 contiguous bytes of each).
 //
-// Per page: Q K^T is two v_mfma_f32_16x16x32_bf16 (bf16 products are exact in
-// FP32, and the sums are FP32), laid out so that every lane receives the 4
-// heads' logits of its own token.  Each of the 16 token streams (slot t of
-// every page of the chunk; the 4 lane rows hold copies) then runs its own
-// FP32 online softmax, with a running maximum that is raised only when a
-// logit exceeds it by more than kRescaleSlack (base-2 units; values p =
-// 2^(x - m) stay below 2^kRescaleSlack, so nothing overflows), and adds p
-// times its V dims with FP32 FMAs.  At the end of the chunk the 16 streams
-// are merged with the log-sum-exp rule by DPP inside each row, the 4 waves of
-// the workgroup the same way through LDS, and the workgroup writes the
-// normalised output (S = 1) or one partial (max, sum, 64-wide accumulator) per
-// query head for the combine kernel (S > 1).
+// Per page (consume_page): S^T = K Q^T is two v_mfma_f32_16x16x32_bf16, the
+// page's K being the A operand as loaded, which leaves lane l with head
+// l & 3's logits of tokens 4*c4 .. 4*c4+3.  The FP32 online softmax keeps one
+// running maximum per head for the whole wave, raised only when a logit
+// exceeds it by more than kRescaleSlack (base-2 units; values p = 2^(x - m)
+// stay below 2^kRescaleSlack, so nothing overflows).  The lane's 4 weights
+// are exactly the A operand of a v_mfma_f32_16x16x16_bf16 over the page's 16
+// tokens; V reaches the B operand through the wave's LDS tile and the
+// transposing read ds_read_b64_tr_b16, and the product sums over the tokens
+// inside the matrix core.  So at the end of a chunk only the 4 lane rows'
+// weight sums need adding; the 4 waves of the workgroup are merged with the
+// log-sum-exp rule through LDS, and the workgroup writes the normalised
+// output (S = 1) or one partial (max, sum, 64-wide accumulator) per query
+// head for the combine kernel (S > 1).
 
 constexpr float kRescaleSlack = 8.0f;
 #ifndef PKV_RING
-#define PKV_RING 4
+#define PKV_RING 3
 #endif
 constexpr int kRing = PKV_RING;  // page buffers per wave: kRing-1 pages in flight
 static_assert(kRing >= 2 && kRing <= 8, "ring size");
@@ -360,10 +357,14 @@ struct PageRegs {
     uint4 ka, kb, va, vb;
 };
 
-struct SoftmaxState {
-    float m[kGroup];
-    float l[kGroup];
-    float acc[kGroup][16];
+// A wave's running state.  Lane l serves query head l & 3 for the logits
+// and the weights (tokens 4c..4c+3 of each page, c = l >> 4), and holds the
+// weighted V sums of all 4 heads for dims 16T + (l & 15) (the same on the 4
+// lane groups c).
+struct WaveState {
+    float m;          // running maximum (base 2) of head l & 3, the same on all its lanes
+    float l;          // sum of this lane's weights (its 4 tokens of every page so far)
+    f32x4_t o[4];     // o[T][i]: head i, dim 16T + (l & 15)
 };
 
 // Buffer descriptor for one (page, KV head) tile: 48-bit base, raw
@@ -415,63 +416,120 @@ struct PageRing {
 };
 
 struct QRegs {
-    bf16x8_t a, b;   // A operands: query head (lane & 3), dims 8c..8c+7 / 32+8c..32+8c+7
+    bf16x8_t a, b;   // B operands: query head (lane & 3), dims 8c..8c+7 / 32+8c..32+8c+7
 };
 
-template <bool kMasked>
-__device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float scale_log2,
-                                             bool valid, SoftmaxState& st) {
-    // S = Q K^T on the matrix cores: A = the 4 query heads repeated over the
-    // 16 rows, B = this page's K (column = token = lane & 15, k = the lane's 8
-    // dims); row 4(lane>>4)+r of the result is head r, so every lane gets the
-    // 4 heads' logits of its token.
-    f32x4_t acc4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a, __builtin_bit_cast(bf16x8_t, pg.ka), acc4, 0, 0, 0);
-    acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.b, __builtin_bit_cast(bf16x8_t, pg.kb), acc4, 0, 0, 0);
-    float x[kGroup];
-#pragma unroll
-    for (int r = 0; r < kGroup; ++r) x[r] = acc4[r] * scale_log2;
-    if (kMasked) {
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) x[r] = valid ? x[r] : -INFINITY;
-        pg.va = valid ? pg.va : make_uint4(0, 0, 0, 0);
-        pg.vb = valid ? pg.vb : make_uint4(0, 0, 0, 0);
+// Where a wave keeps the page it consumes in LDS (BF16 rows padded to
+// kTileRow, so that the 64 lanes of a store or a transposing read spread
+// over the banks), and the lane's offsets into it.
+constexpr int kTileRow = kHeadDim + 8;
+struct PageCtx {
+    uint16_t* vt;        // this wave's V tile [16 tokens][kTileRow]
+    uint16_t* kt;        // this wave's K tile (fused kernel only)
+    int w_off;           // row t, dims 8c..8c+7 (+32 for the second half)
+    int tr_off;          // row 4c + j/4, dims 4(j%4).. (+16T for tile T): the transposing read
+    int lane;
+    int c;               // lane >> 4: this lane's tokens 4c..4c+3
+    int slot;            // fused: the appended token's slot in its page
+    const uint32_t* new_k;   // fused: its rotated K row in LDS (BF16 pairs)
+    const uint32_t* new_v;   // fused: its V row in LDS
+};
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Max over the lanes that serve the same query head (lane bits 2..5).
+__device__ __forceinline__ float head_max(float x) {
+    x = fmaxf(x, dpp<kDppRowRor4>(x));
+    x = fmaxf(x, dpp<kDppRowRor8>(x));
+    return cross_rows_max(x);
+}
+
+// One page: the logits of the 4 query heads for its 16 tokens on the matrix
+// cores (S^T = K Q^T: A = the page's K, column k = the lane's 8 dims; B = the
+// 4 query heads repeated over the 16 columns), so lane l receives head
+// l & 3's logits of tokens 4c..4c+3; the FP32 online softmax with one
+// running maximum per head for the whole wave; the weights p, each split
+// into two BF16 terms hi + lo (p - (hi + lo) is below 2^-17 p), times V on
+// the matrix cores, which sums over the page's tokens (A = the weights,
+// B = V transposed through LDS); products exact, sums in FP32.
+//   kMasked: tokens 4c+i >= valid are left out (their V rows are zeroed in
+//   LDS, so that a NaN-poisoned slot adds nothing); patch (fused kernel):
+//   this page holds the token appended in this launch, whose K and V rows
+//   are taken from LDS (what the page held when it was loaded may predate
+//   the append).
+template <bool kMasked, bool kFused>
+__device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float scale_log2, int valid,
+                                             bool patch, const PageCtx& cx, WaveState& st) {
+    const int t = cx.lane & 15;
+    if (kMasked && t >= valid) {
+        pg.va = make_uint4(0, 0, 0, 0);
+        pg.vb = make_uint4(0, 0, 0, 0);
     }
-    // Largest excess of a new logit over its running maximum (NaN-free: a
-    // masked logit is -inf and m is finite or -inf, and -inf - -inf only
-    // occurs for a masked slot whose stream has seen nothing, which excess
-    // ignores because fmaxf drops the NaN).
-    float excess = x[0] - st.m[0];
+    *reinterpret_cast<uint4*>(cx.vt + cx.w_off) = pg.va;
+    *reinterpret_cast<uint4*>(cx.vt + cx.w_off + 32) = pg.vb;
+    uint4 ka = pg.ka, kb = pg.kb;
+    if constexpr (kFused) {
+        *reinterpret_cast<uint4*>(cx.kt + cx.w_off) = pg.ka;
+        *reinterpret_cast<uint4*>(cx.kt + cx.w_off + 32) = pg.kb;
+        if (patch && cx.lane < 16) {
+            const int i8 = (cx.lane & 7) * 8;
+            const uint4 val = *reinterpret_cast<const uint4*>((cx.lane < 8 ? cx.new_k : cx.new_v) + i8 / 2);
+            *reinterpret_cast<uint4*>((cx.lane < 8 ? cx.kt : cx.vt) + cx.slot * kTileRow + i8) = val;
+        }
+        compiler_fence();   // LDS operations of one wave complete in order
+        ka = *reinterpret_cast<const uint4*>(cx.kt + cx.w_off);
+        kb = *reinterpret_cast<const uint4*>(cx.kt + cx.w_off + 32);
+    }
+    f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), q.a, s4, 0, 0, 0);
+    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), q.b, s4, 0, 0, 0);
+    float x[4];
 #pragma unroll
-    for (int r = 1; r < kGroup; ++r) excess = fmaxf(excess, x[r] - st.m[r]);
+    for (int i = 0; i < 4; ++i) {
+        x[i] = s4[i] * scale_log2;
+        if (kMasked) x[i] = 4 * cx.c + i < valid ? x[i] : -INFINITY;
+    }
+    // Largest excess of a logit over the running maximum (NaN-free: m is
+    // finite or -inf, and -inf - -inf only occurs for a masked token before
+    // any valid one, which fmaxf drops).
+    const float excess = fmaxf(fmaxf(x[0] - st.m, x[1] - st.m), fmaxf(x[2] - st.m, x[3] - st.m));
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(excess > kRescaleSlack) != 0, 0)) {
+        const float pm = head_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool up = pm > st.m + kRescaleSlack;
+        const float alpha = up ? exp2_fast(st.m - pm) : 1.0f;   // 0 when m was -inf
+        st.l *= alpha;
+        st.m = up ? pm : st.m;
+        // o[T][i] belongs to head i, whose factor sits on lane i of each quad.
+        const float a0 = dpp<kDppQuadBcast0>(alpha), a1 = dpp<kDppQuadBcast1>(alpha);
+        const float a2 = dpp<kDppQuadBcast2>(alpha), a3 = dpp<kDppQuadBcast3>(alpha);
 #pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-            // Only heads whose logit jumped rescale; the others keep alpha = 1
-            // (their m may still be -inf, and -inf - -inf must not be formed).
-            const bool up = x[r] > st.m[r] + kRescaleSlack;  // x finite here
-            const float alpha = up ? exp2_fast(st.m[r] - x[r]) : 1.0f;  // 0 when m was -inf
-            st.l[r] *= alpha;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) st.acc[r][k] *= alpha;
-            st.m[r] = up ? x[r] : st.m[r];
+        for (int T = 0; T < 4; ++T) {
+            st.o[T][0] *= a0;
+            st.o[T][1] *= a1;
+            st.o[T][2] *= a2;
+            st.o[T][3] *= a3;
         }
     }
-    const uint32_t vw[8] = {pg.va.x, pg.va.y, pg.va.z, pg.va.w, pg.vb.x, pg.vb.y, pg.vb.z, pg.vb.w};
-    float vf[16];
+    f32x4_t p;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        vf[2 * w] = bf16_lo(vw[w]);
-        vf[2 * w + 1] = bf16_hi(vw[w]);
+    for (int i = 0; i < 4; ++i) {
+        p[i] = exp2_fast(x[i] - st.m);
+        if (kMasked) p[i] = 4 * cx.c + i < valid ? p[i] : 0.0f;
     }
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    const bf16x4_t hi = __builtin_convertvector(p, bf16x4_t);
+    const f32x4_t rest = p - __builtin_convertvector(hi, f32x4_t);
+    const bf16x4_t lo = __builtin_convertvector(rest, bf16x4_t);
+    const s16x4_t ahi = __builtin_bit_cast(s16x4_t, hi), alo = __builtin_bit_cast(s16x4_t, lo);
+    compiler_fence();
 #pragma unroll
-    for (int r = 0; r < kGroup; ++r) {
-        float pr = exp2_fast(x[r] - st.m[r]);
-        if (kMasked) pr = valid ? pr : 0.0f;
-        st.l[r] += pr;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) st.acc[r][k] = fmaf(pr, vf[k], st.acc[r][k]);
+    for (int T = 0; T < 4; ++T) {
+        const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(cx.vt + cx.tr_off + 16 * T));
+        st.o[T] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, v, st.o[T], 0, 0, 0);
+        st.o[T] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, v, st.o[T], 0, 0, 0);
     }
+    compiler_fence();   // the next page's tile stores come after these reads
 }
 
 // A round is kRing straight-line steps (unrolled by template recursion, so
@@ -479,46 +537,29 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float 
 // of a round: slots 0..kRing-2 hold pages j..j+kRing-2 (issued), slot
 // kRing-1 is free.  Step I issues page j+kRing-1 into the slot freed by the
 // previous step, then consumes slot I.
-template <int I, typename Issue>
+template <bool kFused, int I, typename Issue>
 __device__ __forceinline__ void ring_round(PageRing& ring, int& j, const QRegs& q, float sl2,
-                                           SoftmaxState& st, Issue& issue) {
+                                           const PageCtx& cx, WaveState& st, Issue& issue) {
     if constexpr (I < kRing) {
         ring.template at<(I + kRing - 1) % kRing>() = issue(j + kRing - 1);
-        consume_page<false>(ring.template at<I>(), q, sl2, true, st);
+        consume_page<false, kFused>(ring.template at<I>(), q, sl2, kPageTokens, false, cx, st);
         ++j;
-        ring_round<I + 1>(ring, j, q, sl2, st, issue);
+        ring_round<kFused, I + 1>(ring, j, q, sl2, cx, st, issue);
     }
 }
 
-// The new token of a fused append: the page that holds it (-1: none in
-// this launch), its slot, and its rotated K and its V row in LDS (BF16
-// pairs, 32 words each).
-struct NewToken {
-    int page;
-    int slot;
-    const uint32_t* k_row;
-    const uint32_t* v_row;
-};
-
 // The last 1..kRing pages of a chunk sit in slots 0..left-1; they are
-// consumed with the slot mask (only the chunk's last page can be partial).
-// The new token, when this launch appends it, is the last valid slot of the
-// sequence's last page and so of a tail; there its slot is masked (what the
-// page held when it was loaded may predate the append), and the wave then
-// consumes the token from LDS in one more masked step.  A masked slot
-// leaves its stream's state bit for bit unchanged, and the token is the last
-// one its stream sees either way, so the result is the one of a separate
-// append followed by the attention.
-template <int I>
-__device__ __forceinline__ void ring_tail(PageRing& ring, int j, int left, int n, int t,
-                                          const QRegs& q, float sl2, const NewToken& nt,
-                                          SoftmaxState& st) {
+// consumed with the token mask (only the chunk's last page can be partial).
+// tok_page: the page that holds the token appended by a fused call (-1:
+// none).
+template <bool kFused, int I>
+__device__ __forceinline__ void ring_tail(PageRing& ring, int j, int left, int n, const QRegs& q,
+                                          float sl2, int tok_page, const PageCtx& cx, WaveState& st) {
     if constexpr (I < kRing) {
         if (I < left) {
-            const bool stale = j + I == nt.page && t == nt.slot;
-            consume_page<true>(ring.template at<I>(), q, sl2,
-                               t < n - (j + I) * kPageTokens && !stale, st);
-            ring_tail<I + 1>(ring, j, left, n, t, q, sl2, nt, st);
+            consume_page<true, kFused>(ring.template at<I>(), q, sl2, n - (j + I) * kPageTokens,
+                                       j + I == tok_page, cx, st);
+            ring_tail<kFused, I + 1>(ring, j, left, n, q, sl2, tok_page, cx, st);
         }
     }
 }
@@ -554,6 +595,9 @@ void attn_split_kernel(AttnParams p) {
     __shared__ float2 lds_ml[kChunkWaves][kGroup];
     // Fused append: each wave's new rows (BF16 pairs) [q head 0..3, K, V].
     __shared__ __align__(16) uint32_t lds_rot[kFused ? kChunkWaves : 1][kRotRows * kHeadDim / 2];
+    // Each wave's current page: V (and, fused, K) rows of its 16 tokens.
+    __shared__ __align__(16) uint16_t lds_vt[kChunkWaves][kPageTokens * kTileRow];
+    __shared__ __align__(16) uint16_t lds_kt[kFused ? kChunkWaves : 1][kPageTokens * kTileRow];
 
     const int lane = threadIdx.x & 63;
     const int w = uniform((int)(threadIdx.x >> 6));
@@ -594,12 +638,13 @@ void attn_split_kernel(AttnParams p) {
     // position inside the RoPE table); otherwise q is used as given.
     const int pos = ctx - 1;
     const bool rotate = kFused && ctx >= 1 && pos < p.max_pos;
-    // After the wave merge: 4 sums of head 2*b3+b2 (b = bits of t), dims
-    // 32*b1 + 8*c4 + 4*b0 .. +3, and that head's (max, sum).
-    f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f};
-    float mrow = -INFINITY, lsum = 0.0f;
-    const bool b3 = (t & 8) != 0, b2 = (t & 4) != 0, b1 = (t & 2) != 0, b0 = (t & 1) != 0;
-    const int head = (b3 ? 2 : 0) + (b2 ? 1 : 0);
+    // The chunk's result: o[T][i] = head i, dim 16T + (lane & 15); and head
+    // lane & 3's (max, sum).
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) st.o[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     bool bad_page = false;
 
     const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
@@ -629,12 +674,18 @@ void attn_split_kernel(AttnParams p) {
     // j+kRing-1 are in flight.  The last page of the chunk is the only
     // one that can hold slots past n, so it is consumed with the mask.
     PageRing ring;
-    NewToken nt;
-    nt.page = -1;
-    nt.slot = -1;
+    int tok_page = -1;   // fused: the page of the token appended in this launch, when attended
     uint32_t* rot = lds_rot[kFused ? w : 0];
-    nt.k_row = rot + kGroup * 32;
-    nt.v_row = rot + (kGroup + 1) * 32;
+    PageCtx cx;
+    cx.vt = lds_vt[w];
+    cx.kt = lds_kt[kFused ? w : 0];
+    cx.w_off = t * kTileRow + c4 * 8;
+    cx.tr_off = (4 * c4 + ((lane & 15) >> 2)) * kTileRow + 4 * (lane & 3);
+    cx.lane = lane;
+    cx.c = c4;
+    cx.slot = pos & (kPageTokens - 1);
+    cx.new_k = rot + kGroup * 32;
+    cx.new_v = rot + (kGroup + 1) * 32;
     if constexpr (kFused) {
         // Fused append, part 1: the 48 row tasks, one per lane (lanes past
         // 47 repeat the last one).  Their inputs are requested before the
@@ -660,84 +711,39 @@ void attn_split_kernel(AttnParams p) {
 
         // Fused append, part 2: the wave's lanes take the rotated q rows
         // (LDS ops of one wave complete in order; the fences keep the
-        // compiler from moving the reads above the writes); wave 0 of outer
-        // chunk 0 stores the new K/V row where append_kernel would.  The
-        // attention reads the new token from LDS when it was appended and
-        // lies inside the attended length.
+        // compiler from moving the reads above the writes).  When the new
+        // token lies inside the attended length, the page that holds it
+        // takes the token's K and V rows from LDS (consume_page).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + c4 * 4]));
         q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + 16 + c4 * 4]));
-        if (rotate && ctx == n) {
-            nt.page = np - 1;
-            nt.slot = pos & (kPageTokens - 1);
-        }
+        if (rotate && ctx == n) tok_page = np - 1;
     }
 
     if (pb < pe) {
         if constexpr (!kFused) ring_fill<0>(ring, pb, issue);
-        SoftmaxState st;
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-            st.m[r] = -INFINITY;
-            st.l[r] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) st.acc[r][k] = 0.0f;
-        }
         const float sl2 = p.scale_log2;
-
         int j = pb;
         const int rounds = (pe - 1 - pb) / kRing;   // whole rounds of unmasked pages
-        for (int r = 0; r < rounds; ++r) ring_round<0>(ring, j, q, sl2, st, issue);
+        for (int r = 0; r < rounds; ++r) ring_round<kFused, 0>(ring, j, q, sl2, cx, st, issue);
         ring.template at<kRing - 1>() = issue(j + kRing - 1);
-        ring_tail<0>(ring, j, pe - j, n, t, q, sl2, nt, st);
-        if constexpr (kFused) {
-            if (nt.page >= pb && nt.page < pe) {
-                PageRegs pg;
-                pg.ka = *reinterpret_cast<const uint4*>(nt.k_row + c4 * 4);
-                pg.kb = *reinterpret_cast<const uint4*>(nt.k_row + 16 + c4 * 4);
-                pg.va = *reinterpret_cast<const uint4*>(nt.v_row + c4 * 4);
-                pg.vb = *reinterpret_cast<const uint4*>(nt.v_row + 16 + c4 * 4);
-                consume_page<true>(pg, q, sl2, t == nt.slot, st);
-            }
-        }
-
-        // ---- merge the 16 token streams of each row (log-sum-exp rule) ----
-        float M[kGroup], Ls[kGroup];
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) M[r] = row_max(st.m[r]);  // finite: slot pb*16 is valid
-#pragma unroll
-        for (int r = 0; r < kGroup; ++r) {
-            const float alpha = st.m[r] == -INFINITY ? 0.0f : exp2_fast(st.m[r] - M[r]);
-            Ls[r] = row_sum(st.l[r] * alpha);
-#pragma unroll
-            for (int k = 0; k < 16; ++k) st.acc[r][k] *= alpha;
-        }
-        // Reduce-scatter over the row in 4 pair steps (partners t^8, t^7, t^3,
-        // t^1, which together reach all 16 lanes once): heads by b3 then b2,
-        // then the dim half by b1 and the dim quarter by b0.
-        float v1[2][16], v2[16], v3[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int k = 0; k < 16; ++k) v1[h][k] = keep_add<kDppRowRor8>(st.acc[h][k], st.acc[h + 2][k], b3);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) v2[k] = keep_add<kDppRowHalfMirror>(v1[0][k], v1[1][k], b2);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v3[k] = keep_add<kDppQuadRev>(v2[k], v2[k + 8], b1);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) u[k] = keep_add<kDppQuadXor1>(v3[k], v3[k + 4], b0);
-        mrow = head == 0 ? M[0] : head == 1 ? M[1] : head == 2 ? M[2] : M[3];
-        lsum = head == 0 ? Ls[0] : head == 1 ? Ls[1] : head == 2 ? Ls[2] : Ls[3];
-        if (bad_page) lsum = NAN;
+        ring_tail<kFused, 0>(ring, j, pe - j, n, q, sl2, tok_page, cx, st);
+        // The sum of head lane & 3 over the 4 lane rows (their tokens differ).
+        st.l = cross_rows_sum(st.l);
+        if (bad_page) st.l = NAN;
     }
 
     // ---- merge the 4 chunks of the workgroup through LDS ----
     {
-        const int dim0 = (b1 ? 32 : 0) + c4 * 8 + (b0 ? 4 : 0);
-        *reinterpret_cast<float4*>(&lds_acc[w][head][dim0]) = make_float4(u[0], u[1], u[2], u[3]);
-        if (c4 == 0 && (t & 3) == 0) lds_ml[w][head] = make_float2(mrow, lsum);
+        // Lane row c4 stores head c4 (every row holds all 4 heads).
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const float v = c4 == 0 ? st.o[T][0] : c4 == 1 ? st.o[T][1] : c4 == 2 ? st.o[T][2] : st.o[T][3];
+            lds_acc[w][c4][16 * T + (lane & 15)] = v;
+        }
+        if (lane < kGroup) lds_ml[w][lane] = make_float2(st.m, st.l);
     }
     __syncthreads();
     // Wave w finishes query head 4g + w; lane = output dim.
