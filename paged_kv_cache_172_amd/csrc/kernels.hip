@@ -325,8 +325,10 @@ __global__ __launch_bounds__(kCopyThreads) void copy_pages_kernel(CopyParams p) 
 // 4*S chunks of ceil(np / (4*S)) pages and wave w takes chunk 4*ci + w, so the
 // chunk boundaries follow each sequence's own length.  Inside a page, lane l
 // loads the dims [8*c4, 8*c4+8) and [32+8*c4, 32+8*c4+8), c4 = l >> 4, of
-// token slot l & 15's K and V row (two 16-byte loads each; the 16 lanes of a
-// row read 16 token rows, 4 rows of lanes cover 64 contiguous bytes of each).
+// token slot l & 15's K row, the layout of the matrix-core operand below, and
+// the same dims, c4 = l & 3, of token slot l >> 2's V row, so that 4
+// consecutive lanes read 64 contiguous bytes (V passes through LDS anyway;
+// for pages in cache that halves the time).
 //
 // Per page (consume_page): S^T = K Q^T is two v_mfma_f32_16x16x32_bf16, the
 // page's K being the A operand as loaded, which leaves lane l with head
@@ -387,12 +389,12 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 __device__ __forceinline__ PageRegs load_page(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                              uint32_t off_a, uint32_t off_b) {
+                                              uint32_t k_off, uint32_t v_off) {
     PageRegs r;
-    r.ka = buffer_load16(kr, off_a);
-    r.kb = buffer_load16(kr, off_b);
-    r.va = buffer_load16(vr, off_a);
-    r.vb = buffer_load16(vr, off_b);
+    r.ka = buffer_load16(kr, k_off);
+    r.kb = buffer_load16(kr, k_off + 64);
+    r.va = buffer_load16(vr, v_off);
+    r.vb = buffer_load16(vr, v_off + 64);
     return r;
 }
 
@@ -426,7 +428,8 @@ constexpr int kTileRow = kHeadDim + 8;
 struct PageCtx {
     uint16_t* vt;        // this wave's V tile [16 tokens][kTileRow]
     uint16_t* kt;        // this wave's K tile (fused kernel only)
-    int w_off;           // row t, dims 8c..8c+7 (+32 for the second half)
+    int w_off;           // V as loaded: row l >> 2, dims 8(l & 3).. (+32 for the second half)
+    int k_off;           // K as the MFMA takes it: row l & 15, dims 8c.. (+32)
     int tr_off;          // row 4c + j/4, dims 4(j%4).. (+16T for tile T): the transposing read
     int lane;
     int c;               // lane >> 4: this lane's tokens 4c..4c+3
@@ -460,8 +463,7 @@ __device__ __forceinline__ float head_max(float x) {
 template <bool kMasked, bool kFused>
 __device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float scale_log2, int valid,
                                              bool patch, const PageCtx& cx, WaveState& st) {
-    const int t = cx.lane & 15;
-    if (kMasked && t >= valid) {
+    if (kMasked && (cx.lane >> 2) >= valid) {
         pg.va = make_uint4(0, 0, 0, 0);
         pg.vb = make_uint4(0, 0, 0, 0);
     }
@@ -469,16 +471,16 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float 
     *reinterpret_cast<uint4*>(cx.vt + cx.w_off + 32) = pg.vb;
     uint4 ka = pg.ka, kb = pg.kb;
     if constexpr (kFused) {
-        *reinterpret_cast<uint4*>(cx.kt + cx.w_off) = pg.ka;
-        *reinterpret_cast<uint4*>(cx.kt + cx.w_off + 32) = pg.kb;
+        *reinterpret_cast<uint4*>(cx.kt + cx.k_off) = pg.ka;
+        *reinterpret_cast<uint4*>(cx.kt + cx.k_off + 32) = pg.kb;
         if (patch && cx.lane < 16) {
             const int i8 = (cx.lane & 7) * 8;
             const uint4 val = *reinterpret_cast<const uint4*>((cx.lane < 8 ? cx.new_k : cx.new_v) + i8 / 2);
             *reinterpret_cast<uint4*>((cx.lane < 8 ? cx.kt : cx.vt) + cx.slot * kTileRow + i8) = val;
         }
         compiler_fence();   // LDS operations of one wave complete in order
-        ka = *reinterpret_cast<const uint4*>(cx.kt + cx.w_off);
-        kb = *reinterpret_cast<const uint4*>(cx.kt + cx.w_off + 32);
+        ka = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off);
+        kb = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off + 32);
     }
     f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
     s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), q.a, s4, 0, 0, 0);
@@ -647,8 +649,10 @@ void attn_split_kernel(AttnParams p) {
     for (int T = 0; T < 4; ++T) st.o[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     bool bad_page = false;
 
-    const uint32_t off_a = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
-    const uint32_t off_b = off_a + 64;
+    // K lands in the MFMA operand layout (row l & 15); V, which passes
+    // through LDS, is loaded 4 lanes per 64 contiguous bytes of a row.
+    const uint32_t k_off = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
+    const uint32_t v_off = (uint32_t)(((lane >> 2) * p.slot_stride + (lane & 3) * 8) * 2);
     const int32_t tile_bytes = (int32_t)((15 * p.slot_stride + kHeadDim) * 2);
     const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
     const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
@@ -666,8 +670,8 @@ void attn_split_kernel(AttnParams p) {
         }
         const int32_t bytes = live ? tile_bytes : 0;
         const int64_t off = (int64_t)phys * page_bytes;
-        return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), off_a,
-                         off_b);
+        return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), k_off,
+                         v_off);
     };
 
     // Ring of kRing page buffers: while page j is consumed, pages j+1 ..
@@ -679,7 +683,8 @@ void attn_split_kernel(AttnParams p) {
     PageCtx cx;
     cx.vt = lds_vt[w];
     cx.kt = lds_kt[kFused ? w : 0];
-    cx.w_off = t * kTileRow + c4 * 8;
+    cx.w_off = (lane >> 2) * kTileRow + (lane & 3) * 8;
+    cx.k_off = t * kTileRow + c4 * 8;
     cx.tr_off = (4 * c4 + ((lane & 15) >> 2)) * kTileRow + 4 * (lane & 3);
     cx.lane = lane;
     cx.c = c4;
