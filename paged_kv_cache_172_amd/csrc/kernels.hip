@@ -439,6 +439,9 @@ struct PageCtx {
 };
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+// Hides where a value came from: the K rows read back from LDS stay in
+// registers instead of the compiler merging them with the ring's slots.
+__device__ __forceinline__ void opaque(uint4& v) { asm("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
 
 // Max over the lanes that serve the same query head (lane bits 2..5).
 __device__ __forceinline__ float head_max(float x) {
@@ -459,7 +462,8 @@ __device__ __forceinline__ float head_max(float x) {
 //   LDS, so that a NaN-poisoned slot adds nothing); patch (fused kernel):
 //   this page holds the token appended in this launch, whose K and V rows
 //   are taken from LDS (what the page held when it was loaded may predate
-//   the append).
+//   the append).  That page is the sequence's last, so only the masked tail
+//   sees it, and only that one page goes through the K tile in LDS.
 template <bool kMasked, bool kFused>
 __device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float scale_log2, int valid,
                                              bool patch, const PageCtx& cx, WaveState& st) {
@@ -470,17 +474,21 @@ __device__ __forceinline__ void consume_page(PageRegs pg, const QRegs& q, float 
     *reinterpret_cast<uint4*>(cx.vt + cx.w_off) = pg.va;
     *reinterpret_cast<uint4*>(cx.vt + cx.w_off + 32) = pg.vb;
     uint4 ka = pg.ka, kb = pg.kb;
-    if constexpr (kFused) {
-        *reinterpret_cast<uint4*>(cx.kt + cx.k_off) = pg.ka;
-        *reinterpret_cast<uint4*>(cx.kt + cx.k_off + 32) = pg.kb;
-        if (patch && cx.lane < 16) {
-            const int i8 = (cx.lane & 7) * 8;
-            const uint4 val = *reinterpret_cast<const uint4*>((cx.lane < 8 ? cx.new_k : cx.new_v) + i8 / 2);
-            *reinterpret_cast<uint4*>((cx.lane < 8 ? cx.kt : cx.vt) + cx.slot * kTileRow + i8) = val;
+    if constexpr (kFused && kMasked) {
+        if (patch) {   // wave-uniform: the page of the token appended in this launch
+            *reinterpret_cast<uint4*>(cx.kt + cx.k_off) = pg.ka;
+            *reinterpret_cast<uint4*>(cx.kt + cx.k_off + 32) = pg.kb;
+            if (cx.lane < 16) {
+                const int i8 = (cx.lane & 7) * 8;
+                const uint4 val = *reinterpret_cast<const uint4*>((cx.lane < 8 ? cx.new_k : cx.new_v) + i8 / 2);
+                *reinterpret_cast<uint4*>((cx.lane < 8 ? cx.kt : cx.vt) + cx.slot * kTileRow + i8) = val;
+            }
+            compiler_fence();   // LDS operations of one wave complete in order
+            ka = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off);
+            kb = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off + 32);
+            opaque(ka);
+            opaque(kb);
         }
-        compiler_fence();   // LDS operations of one wave complete in order
-        ka = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off);
-        kb = *reinterpret_cast<const uint4*>(cx.kt + cx.k_off + 32);
     }
     f32x4_t s4 = {0.0f, 0.0f, 0.0f, 0.0f};
     s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), q.a, s4, 0, 0, 0);
@@ -740,6 +748,31 @@ void attn_split_kernel(AttnParams p) {
         if (bad_page) st.l = NAN;
     }
 
+    if constexpr (kFused) {
+        // Fused append, part 3: wave 0 of outer chunk 0 stores the new K/V
+        // row where append_kernel would.  After the page loop: a store counts
+        // against the same in-order memory counter as the page loads, so an
+        // earlier one would hold back this wave's waits for its pages; here
+        // none are left, and the write overlaps the merge below.
+        if (rotate && ci == 0 && w == 0 && lane < 16) {
+            const int64_t jpage = pos >> 4;
+            if (jpage < p.bt_stride) {
+                // From the table registers when the entry is among the first 128.
+                const int64_t page = jpage < bt_w ? (jpage < 64 ? __builtin_amdgcn_readlane(tbl0, (int)jpage)
+                                                                : __builtin_amdgcn_readlane(tbl1, (int)jpage - 64))
+                                                  : bt_row[jpage];
+                if (page >= 0 && page < p.num_pages) {   // never write through a bad entry
+                    const int64_t dst = page * p.page_stride + g * p.head_stride +
+                                        (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
+                    const int i8 = (lane & 7) * 8;
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        &rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
+                    *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
+                }
+            }
+        }
+    }
+
     // ---- merge the 4 chunks of the workgroup through LDS ----
     {
         // Lane row c4 stores head c4 (every row holds all 4 heads).
@@ -775,29 +808,6 @@ void attn_split_kernel(AttnParams p) {
         const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + ci;
         p.ws_acc[slot_idx * kHeadDim + lane] = o;
         if (lane == 0) p.ws_ml[slot_idx] = make_float2(Mx, L);
-    }
-    if constexpr (kFused) {
-        // Fused append, part 3: wave 0 of outer chunk 0 stores the new K/V
-        // row where append_kernel would.  Last, next to the output: a store
-        // counts against the same in-order memory counter as the page loads,
-        // so an early one would hold back this wave's waits for its pages.
-        if (rotate && ci == 0 && w == 0 && lane < 16) {
-            const int64_t jpage = pos >> 4;
-            if (jpage < p.bt_stride) {
-                // From the table registers when the entry is among the first 128.
-                const int64_t page = jpage < bt_w ? (jpage < 64 ? __builtin_amdgcn_readlane(tbl0, (int)jpage)
-                                                                : __builtin_amdgcn_readlane(tbl1, (int)jpage - 64))
-                                                  : bt_row[jpage];
-                if (page >= 0 && page < p.num_pages) {   // never write through a bad entry
-                    const int64_t dst = page * p.page_stride + g * p.head_stride +
-                                        (int64_t)(pos & (kPageTokens - 1)) * p.slot_stride;
-                    const int i8 = (lane & 7) * 8;
-                    const uint4 val = *reinterpret_cast<const uint4*>(
-                        &rot[(lane < 8 ? kGroup : kGroup + 1) * 32 + i8 / 2]);
-                    *reinterpret_cast<uint4*>((lane < 8 ? p.k_pool_w : p.v_pool_w) + dst + i8) = val;
-                }
-            }
-        }
     }
 }
 
