@@ -74,79 +74,128 @@ __device__ __forceinline__ T uniform(T x) {
 
 // ------------------------------------------------------------- append --
 
-// Round an FP64 value to the nearest BF16 bit pattern, ties to even, in one
-// step from the FP64 bits (no intermediate FP32 rounding).
-__device__ __forceinline__ uint32_t f64_to_bf16_rne_slow(uint64_t u) {
-    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-    const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
-    if (mag > 0x7FF0000000000000ull) return sign | 0x7FC0u;  // NaN
-    const int e = (int)(mag >> 52);                          // biased FP64 exponent
-    if (e >= 1023 + 128) return sign | 0x7F80u;              // |y| >= 2^128 (or inf)
-    const uint64_t sig = (mag & 0x000FFFFFFFFFFFFFull) | (e ? (1ull << 52) : 0ull);
-    // Keep `shift` low bits out: 45 for a normal BF16 result (8 significant
-    // bits of 53), more below 2^-126 where the BF16 grid step is 2^-133.
-    int shift = 45;
-    int eb = e - 1023 + 127;                                 // BF16 biased exponent
-    if (eb < 1) {
-        shift = 45 + (1 - eb);
-        eb = 0;
-    }
-    if (shift >= 54) return sign;                            // below half the smallest subnormal
-    uint64_t kept = sig >> shift;
-    const uint64_t rem = sig & ((1ull << shift) - 1);
-    const uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (kept & 1))) ++kept;
-    if (eb == 0) return sign | (uint32_t)kept;               // subnormal (or carried into 0x0080)
-    if (kept == 0x100) {                                     // carried into the next binade
-        kept = 0x80;
-        ++eb;
-        if (eb >= 255) return sign | 0x7F80u;
-    }
-    return sign | ((uint32_t)eb << 7) | ((uint32_t)kept & 0x7Fu);
+// Round an FP64 value to the nearest BF16 bit pattern, ties to even, without
+// branches.  Step 1 rounds to FP32 "to odd": the FP32 value toward zero,
+// with its last bit set when anything was cut off.  Step 2 rounds that to
+// BF16 to nearest, ties to even.  FP32 carries 24 significant bits, more than
+// BF16's 8 + 2, so the two steps give the single rounding's result (Boldo and
+// Melquiond, "When double rounding is odd", 2005); the same holds on the
+// subnormal grids (2^-149 against 2^-133) and for overflow (FP32 max rounds
+// to infinity).  NaN gives the sign with the quiet pattern 0x7FC0.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
+    const float f = (float)y;                         // nearest FP32 (FP32 denormals kept)
+    const double back = (double)f;
+    uint32_t b = __float_as_uint(f);
+    b -= fabs(back) > fabs(y) ? 1u : 0u;              // rounded away from zero: step back
+    b |= back != y ? 1u : 0u;                         // sticky bit
+    const uint32_t r = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+    const uint32_t sign = (uint32_t)(__double_as_longlong(y) >> 48) & 0x8000u;
+    return y != y ? sign | 0x7FC0u : r;
 }
 
-__device__ __forceinline__ uint32_t f64_to_bf16_rne(double y) {
+// The BF16 bits of the nearest value to y, ties to even, for |y| in
+// [2^-126, (2 - 2^-8) 2^127): results that are normal BF16 numbers.  It works
+// on the high word of y's FP64 bits with the low word folded into its last
+// bit (only "nonzero" matters below the rounding bit): add the half-way bias
+// below the 7 kept mantissa bits, and rebias the exponent from 1023 to 127
+// (896 << 20, a multiple of the 2^13 cut, is subtracted before the shift).
+// ok is cleared when y lies outside that range.
+__device__ __forceinline__ uint32_t f64_to_bf16_normal(double y, bool& ok) {
     const uint64_t u = __double_as_longlong(y);
-    const uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
-    // |y| in [2^-126, (2 - 2^-8) * 2^127): the result is a normal BF16.  Add the
-    // round-half-even bias below the 7 kept mantissa bits and rebias the
-    // exponent from 1023 to 127 (a carry into the exponent is the binade step).
-    if (mag >= 0x3810000000000000ull && mag < 0x47EFF00000000000ull) {
-        const uint64_t t = mag + 0x00000FFFFFFFFFFFull + ((mag >> 45) & 1ull);
-        return ((uint32_t)(u >> 48) & 0x8000u) | (uint32_t)((t >> 45) - (896ull << 7));
-    }
-    return f64_to_bf16_rne_slow(u);
+    const uint32_t hi = (uint32_t)(u >> 32);
+    const uint32_t mag = (hi & 0x7FFFFFFFu) | min((uint32_t)u, 1u);
+    ok = ok && mag - 0x38100000u < 0x47EFF000u - 0x38100000u;
+    const uint32_t r = (mag + (0xFFFu - 0x38000000u) + ((mag >> 13) & 1u)) >> 13;
+    return r | ((hi >> 16) & 0x8000u);
+}
+
+// One rotated element in FP32, u*c - v*s: p = v*s rounded and its exact
+// error e (an FMA); r = u*c - p rounded; y = r - e rounded.  Then
+// |y - (u c - v s)| <= ulp(r)/2 + ulp(y)/2 + 2^-150 (the last term if e
+// underflowed), at most 2 ulp(y) when |r| <= 2|y| and y is normal.  y then
+// rounds to BF16 as the exact value (and its FP64 rounding) does when y lies
+// at least 3 FP32 ulps from every BF16 half-way point: its low 16 bits
+// outside 0x8000 +- 2 (points across a binade edge lie 2^15 ulps away or
+// more).  The caller folds the three conditions over its elements:
+//   margin: the minimum of (bits(y) << 16) + 0x80020000 is >= 5 << 16;
+//   slack:  the minimum of 2|y| - |r| is >= 0 (its sign is exact);
+//   normal: every y is a normal number.
+struct RotCheck {
+    uint32_t margin = 0xFFFFFFFFu;
+    float slack = INFINITY;
+    bool normal = true;
+};
+__device__ __forceinline__ float rot_f32(float u, float c, float v, float s, RotCheck& k) {
+#pragma clang fp contract(off)
+    const float p = v * s;
+    const float e = __builtin_fmaf(v, s, -p);
+    const float r = __builtin_fmaf(u, c, -p);
+    const float y = r - e;
+    k.margin = min(k.margin, (__float_as_uint(y) << 16) + 0x80020000u);
+    k.slack = fminf(k.slack, __builtin_fmaf(2.0f, fabsf(y), -fabsf(r)));
+    k.normal = k.normal && __builtin_isnormal(y);
+    return y;
 }
 
 // Rotate the 4 pairs (i0+e, i0+e+32), e < 4, of one head vector with the
-// table row of the new token's position, in FP64, and round each result once
-// to BF16.  x1 holds dims i0..i0+3 and x2 dims i0+32..i0+35 as BF16 pairs.
+// table row of the new token's position, and round each result once to BF16
+// as from its FP64 value.  x1 holds dims i0..i0+3 and x2 dims i0+32..i0+35
+// as BF16 pairs.  Three paths, chosen for the whole wave: FP32 with a
+// certainty test (rot_f32); FP64 with the normal-range rounding;
+// FP64 with the general rounding.  Where more than one applies they give
+// the same bits.
 __device__ __forceinline__ void rope4(uint2& x1, uint2& x2, float4 c, float4 sn) {
     const uint32_t a[2] = {x1.x, x1.y};
     const uint32_t b[2] = {x2.x, x2.y};
     const float cs[4] = {c.x, c.y, c.z, c.w};
     const float ss[4] = {sn.x, sn.y, sn.z, sn.w};
-    uint32_t ya[2], yb[2];
+    float u1[4], u2[4];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        uint32_t lo_a = 0, lo_b = 0;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int e = 2 * w + half;
-            const double u1 = (double)(half ? bf16_hi(a[w]) : bf16_lo(a[w]));
-            const double u2 = (double)(half ? bf16_hi(b[w]) : bf16_lo(b[w]));
-            const double cc = (double)cs[e];
-            const double s = (double)ss[e];
-            // Both products are exact in FP64 (8 x 24 significant bits), so
-            // each line rounds once, whatever the compiler contracts.
-            lo_a |= f64_to_bf16_rne(u1 * cc - u2 * s) << (16 * half);
-            lo_b |= f64_to_bf16_rne(u2 * cc + u1 * s) << (16 * half);
-        }
-        ya[w] = lo_a;
-        yb[w] = lo_b;
+    for (int e = 0; e < 4; ++e) {
+        u1[e] = (e & 1) ? bf16_hi(a[e >> 1]) : bf16_lo(a[e >> 1]);
+        u2[e] = (e & 1) ? bf16_hi(b[e >> 1]) : bf16_lo(b[e >> 1]);
     }
-    x1 = make_uint2(ya[0], ya[1]);
-    x2 = make_uint2(yb[0], yb[1]);
+    RotCheck k;
+    f32x4_t fa, fb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        fa[e] = rot_f32(u1[e], cs[e], u2[e], ss[e], k);      // u1 c - u2 s
+        fb[e] = rot_f32(u2[e], cs[e], -u1[e], ss[e], k);     // u2 c + u1 s
+    }
+    const bool certain = k.normal && k.margin >= 0x50000u && k.slack >= 0.0f;
+    if (__builtin_amdgcn_ballot_w64(!certain) == 0) {   // wave-uniform
+        const uint2 ba = __builtin_bit_cast(uint2, __builtin_convertvector(fa, bf16x4_t));
+        const uint2 bb = __builtin_bit_cast(uint2, __builtin_convertvector(fb, bf16x4_t));
+        x1 = ba;
+        x2 = bb;
+        return;
+    }
+    double ya[4], yb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double d1 = (double)u1[e], d2 = (double)u2[e];
+        const double cc = (double)cs[e], s = (double)ss[e];
+        // Both products are exact in FP64 (8 x 24 significant bits), so
+        // each line rounds once, whatever the compiler contracts.
+        ya[e] = d1 * cc - d2 * s;
+        yb[e] = d2 * cc + d1 * s;
+    }
+    uint32_t ra[4], rb[4];
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ra[e] = f64_to_bf16_normal(ya[e], ok);
+        rb[e] = f64_to_bf16_normal(yb[e], ok);
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok) != 0) {   // wave-uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ra[e] = f64_to_bf16_rne(ya[e]);
+            rb[e] = f64_to_bf16_rne(yb[e]);
+        }
+    }
+    x1 = make_uint2(ra[0] | (ra[1] << 16), ra[2] | (ra[3] << 16));
+    x2 = make_uint2(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16));
 }
 
 // Three 128-thread blocks per group of appended rows; a task is 4 rotation

@@ -229,3 +229,107 @@ def test_prefill_full_size(torch_gpu, orc, rope):
     # every page of the pool that no table names is untouched
     unused = np.setdiff1d(np.arange(num_pages), bt.ravel())
     assert (got_pages[unused] == wl.BF16_NAN).all()
+
+
+def _edge_bf16(rng, shape):
+    """BF16 bit patterns aimed at the rounding of the rotation: mostly short
+    mantissas (so that products land on or near BF16 half-way points), some
+    Gaussian values, and the edges: values near the top of the range,
+    subnormals, zeros, infinities and NaN."""
+    n = int(np.prod(shape))
+    kind = rng.choice(7, size=n, p=[0.62, 0.14, 0.07, 0.06, 0.04, 0.04, 0.03])
+    sign = rng.integers(0, 2, n).astype(np.uint16) << 15
+    short_m = rng.choice(np.array([0, 1, 2, 3, 64, 65, 127], np.uint16), n)
+    mid_e = rng.integers(127 - 20, 127 + 21, n).astype(np.uint16)
+    top_e = rng.integers(250, 255, n).astype(np.uint16)
+    rand_m = rng.integers(0, 128, n).astype(np.uint16)
+    gauss = wl.f32_to_bf16_bits(rng.standard_normal(n, dtype=np.float32))
+    out = np.where(kind == 0, sign | (mid_e << 7) | short_m, 0).astype(np.uint16)
+    out = np.where(kind == 1, gauss, out)
+    out = np.where(kind == 2, sign | (top_e << 7) | rand_m, out)                      # near overflow
+    out = np.where(kind == 3, sign | rng.integers(1, 128, n).astype(np.uint16), out)  # subnormal
+    out = np.where(kind == 4, sign | (rng.integers(1, 4, n).astype(np.uint16) << 7) | rand_m, out)
+    out = np.where(kind == 5, sign, out)                                              # +-0
+    special = rng.choice(np.array([0x7F80, 0xFF80, 0x7FC0, 0x7F7F, 0xFF7F], np.uint16), n)
+    out = np.where(kind == 6, special, out)
+    return out.reshape(shape)
+
+
+def _edge_table(rng, rows):
+    """FP32 cos/sin rows whose products with short BF16 values fall on
+    half-way points, just beside them (an s of 2^-30 moves a half-way point
+    by far less than an FP32 ulp), or outside the FP32 range."""
+    c_set = np.array([1.0, 1.0 + 2.0**-8, 1.0 - 2.0**-9, 0.75, 0.5 + 2.0**-9, 2.0**-20, 0.0,
+                      -1.0, 1.0 + 2.0**-7 + 2.0**-30, 2.0**-126, 2.0**100, -(1.0 + 2.0**-8)],
+                     np.float64).astype(np.float32)
+    s_set = np.array([0.0, 2.0**-30, -2.0**-30, 2.0**-8, -2.0**-8, 2.0**-24, 0.5, 2.0**-100,
+                      1e-40, 2.0**-9 * (1 + 2.0**-23), 2.0**90], np.float64).astype(np.float32)
+    c = rng.choice(c_set, (rows, 32))
+    s = rng.choice(s_set, (rows, 32))
+    mix = rng.random((rows, 32)) < 0.15             # some ordinary entries
+    c = np.where(mix, rng.uniform(-1, 1, (rows, 32)).astype(np.float32), c)
+    s = np.where(mix, rng.uniform(-1, 1, (rows, 32)).astype(np.float32), s)
+    return np.ascontiguousarray(c, np.float32), np.ascontiguousarray(s, np.float32)
+
+
+def _is_nan16(b):
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+
+
+def test_rotation_rounding_edges(torch_gpu, orc, rope):
+    """The rotation's single rounding to BF16 at its edges: exact half-way
+    points (ties to even), values beside a half-way point by less than an
+    FP32 ulp (where rounding first to FP32 would go wrong), overflow to
+    infinity, subnormal results, signed zeros, infinities and NaN, through
+    paged_kv_prefill and paged_kv_append.  Bar: the oracle's bits wherever
+    the oracle's result is a number; NaN where it is NaN (the sign of a NaN
+    made by arithmetic is not portable).  Rows mix these with ordinary rows
+    and table entries, so that every rounding path of the kernels runs."""
+    rng = np.random.Generator(np.random.PCG64(714))
+    edge_c, edge_s = _edge_table(rng, 32)
+    real = orc.rope_table(500000.0, 1032)
+    table = (np.concatenate([edge_c, real[0][1000:1032]]),
+             np.concatenate([edge_s, real[1][1000:1032]]))
+    starts = [0, 0, 0, 0, 32, 32, 32, 0]          # rows at positions 0..31 use the edge table
+    counts = [32] * 8
+    c = make_case(715, starts, counts)
+    T = int(c["cu"][-1])
+    edge_rows = np.concatenate([np.arange(32 * s, 32 * s + 32) for s in (0, 1, 2, 3, 6)])
+    c["q"][edge_rows] = _edge_bf16(rng, (len(edge_rows), 2048))
+    c["k"][edge_rows] = _edge_bf16(rng, (len(edge_rows), 512))
+    c["v"][edge_rows] = _edge_bf16(rng, (len(edge_rows), 512))
+
+    # The inputs hold what the test is about (the oracle and numpy only):
+    # exact ties, and values that a rounding through FP32 would get wrong.
+    ys = []
+    for row in range(T):
+        s = int(np.searchsorted(c["cu"], row, side="right") - 1)
+        pos = int(c["start"][s]) + row - int(c["cu"][s])
+        heads = np.concatenate([c["q"][row].reshape(32, 64), c["k"][row].reshape(8, 64)])
+        for h in heads:
+            ys.append(orc.rope_rotate_f64(oracle.bf16_to_f64(h), table[0][pos], table[1][pos]))
+    y = np.concatenate(ys)
+    with np.errstate(all="ignore"):
+        exact = orc.bf16_round_array(y)
+        y32 = y.astype(np.float32)
+        via_f32 = wl.f32_to_bf16_bits(y32)
+        num = ~np.isnan(y)
+        ties = num & (y32.astype(np.float64) == y) & ((y32.view(np.uint32) & 0xFFFF) == 0x8000)
+    hazards = num & (via_f32 != exact)
+    say(f"[edges] {y.size} rotated values: {int(ties.sum())} exact ties, "
+        f"{int(hazards.sum())} that rounding through FP32 gets wrong, "
+        f"{int((~num).sum())} NaN, {int(np.isinf(y).sum())} infinite")
+    assert ties.sum() >= 100 and hazards.sum() >= 100
+
+    dev = Dev(torch_gpu, c, table)
+    dev.prefill()
+    ref_pages, ref_q = oracle_prefill(orc, c, table)
+    for name, got, ref in (("pages", to_u16(dev.pages).reshape(ref_pages.shape), ref_pages),
+                           ("q", to_u16(dev.q).reshape(ref_q.shape), ref_q)):
+        nan = _is_nan16(ref)
+        assert np.array_equal(_is_nan16(got), nan), name
+        bad = (got != ref) & ~nan
+        assert not bad.any(), f"{name}: {int(bad.sum())} values differ, first at {np.argwhere(bad)[0]}"
+    one = Dev(torch_gpu, c, table)
+    one.appends(c)
+    assert torch_gpu.equal(one.pages, dev.pages) and torch_gpu.equal(one.q, dev.q)
