@@ -39,6 +39,7 @@ Plan make_plan(int32_t num_seqs, int32_t max_context_len) {
     int64_t s = (kTargetWaves + waves_per_split - 1) / waves_per_split;
     const int64_t s_cap = max_pages / ((int64_t)kChunkWaves * kMinPagesPerSplit);
     if (s > s_cap) s = s_cap;
+    if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
     return Plan{(int32_t)s};
 }

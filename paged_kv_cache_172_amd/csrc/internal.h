@@ -72,6 +72,9 @@ struct CopyParams {
 // of kChunkWaves waves; a sequence of np pages is cut into kChunkWaves * S
 // chunks of ceil(np / (kChunkWaves * S)) pages.
 constexpr int kChunkWaves = 4;
+// Outer chunks per sequence at most (the plan caps S here; with contexts of
+// at most 2,048 tokens and 4 pages per wave at least, S <= 8 anyway).
+constexpr int kMaxSplits = 8;
 struct Plan {
     int32_t splits;
 };

@@ -861,7 +861,10 @@ void attn_split_kernel(AttnParams p) {
 }
 
 // One thread per (sequence, query head, 4 output dims): merges the S
-// outer-chunk partials with the log-sum-exp rule (empty ones weigh 0).
+// outer-chunk partials with the log-sum-exp rule (empty ones weigh 0).  All
+// S (max, sum) pairs and accumulator quads are requested at once (an index
+// past S rereads the last partial and is then ignored), so the thread waits
+// for one round trip, not one per partial.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int d4 = (int)(tid & 15);
@@ -870,19 +873,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     if (s >= p.num_seqs) return;
     const int S = p.plan.splits;
     const int64_t base = ((int64_t)s * kQHeads + h) * S;
+    float2 ml[kMaxSplits];
+    float4 v[kMaxSplits];
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) {
+        const int64_t slot = base + (c < S ? c : S - 1);
+        ml[c] = p.ws_ml[slot];
+        v[c] = *reinterpret_cast<const float4*>(p.ws_acc + slot * kHeadDim + d4 * 4);
+    }
+    // Past S every term is an exact 0 (selected, never a product with a
+    // reread partial, which may be NaN), so the sums are those over the S.
     float M = -INFINITY;
-    for (int c = 0; c < S; ++c) M = fmaxf(M, p.ws_ml[base + c].x);
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) M = fmaxf(M, c < S ? ml[c].x : -INFINITY);
     float L = 0.0f;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 0; c < S; ++c) {
-        const float2 ml = p.ws_ml[base + c];
-        const float w = ml.x == -INFINITY ? 0.0f : exp2_fast(ml.x - M);
-        const float4 v = *reinterpret_cast<const float4*>(p.ws_acc + (base + c) * kHeadDim + d4 * 4);
-        L = fmaf(w, ml.y, L);
-        a.x = fmaf(w, v.x, a.x);
-        a.y = fmaf(w, v.y, a.y);
-        a.z = fmaf(w, v.z, a.z);
-        a.w = fmaf(w, v.w, a.w);
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) {
+        const bool in = c < S && ml[c].x != -INFINITY;
+        const float w = in ? exp2_fast(ml[c].x - M) : 0.0f;
+        const float l = c < S ? ml[c].y : 0.0f;
+        const float4 x = c < S ? v[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        L = fmaf(w, l, L);
+        a.x = fmaf(w, x.x, a.x);
+        a.y = fmaf(w, x.y, a.y);
+        a.z = fmaf(w, x.z, a.z);
+        a.w = fmaf(w, x.w, a.w);
     }
     const float inv = L == 0.0f ? 0.0f : 1.0f / L;
     *reinterpret_cast<float4*>(p.out + s * p.out_stride + h * kHeadDim + d4 * 4) =
@@ -926,6 +942,7 @@ hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream) {
+    if (p.plan.splits < 1 || p.plan.splits > kMaxSplits) return hipErrorInvalidValue;   // the plan caps S
     const int64_t threads = (int64_t)p.num_seqs * kQHeads * 16;
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
