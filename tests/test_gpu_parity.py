@@ -171,6 +171,31 @@ def test_page_permutation_is_bitwise_invariant(torch_gpu, rope):
     assert torch_gpu.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["ragged40", "single_chunk400"])
+def test_batch_order_is_bitwise_invariant(torch_gpu, rope, name):
+    """The same sequences in another batch order give the same output rows,
+    permuted, bit for bit: each (sequence, KV head, chunk) is computed the
+    same way whichever workgroup slot serves it.  ragged40 runs S > 1 with
+    the combine; single_chunk400 runs S = 1 with more workgroups than the
+    GPU holds at once, longest sequences first in the second order."""
+    spec = SMALL[name]()
+    hw = wl.make_host_workload(spec)
+    batch = host_batch(hw, rope)
+    batch.append(0)
+    a = _run_attn(batch)
+    perm = np.argsort(-spec.ctx, kind="stable")
+    if name == "ragged40":
+        perm = np.random.default_rng(509).permutation(spec.num_seqs)
+    idx = torch_gpu.from_numpy(perm).to(a.device)
+    batch2 = DecodeBatch(batch.pool_pages, np.ascontiguousarray(spec.block_tables[:, perm]),
+                         np.ascontiguousarray(spec.ctx[perm]), batch.q[:, idx].contiguous(),
+                         np.ascontiguousarray(hw.k[:, perm]), np.ascontiguousarray(hw.v[:, perm]),
+                         rope=rope, max_context_len=int(spec.ctx.max()))
+    assert batch2.splits == batch.splits
+    b = _run_attn(batch2)
+    assert torch_gpu.equal(a[idx], b)
+
+
 def test_poison_is_never_read(torch_gpu, rope):
     """NaN in unused slots, free pages and table tails (-1) changes nothing."""
     spec = wl.make_spec([23, 9, 48, 2000, 1], 1, seed=508, extra_free=7)
