@@ -53,6 +53,17 @@ SMALL = {
 }
 
 
+def _odd_splits(B, seed):
+    """B sequences, one of 2,048 tokens (so the plan sees the full context),
+    the rest uniform in 1..2048: B = 10, 11, 13, 22 give S = 7, 6, 5, 3."""
+    lens = np.random.default_rng(seed).integers(1, 2049, B)
+    lens[0] = 2048
+    return wl.make_spec(lens, 1, seed=seed)
+
+
+SMALL.update({f"odd_splits{B}": (lambda B=B: _odd_splits(B, 510 + B)) for B in (10, 11, 13, 22)})
+
+
 def _oracle_append_all(orc, hw, rope):
     pages = hw.pages.copy()
     q = hw.q.copy()
@@ -141,11 +152,14 @@ def _run_attn(batch, layer=0, two_phase=False):
     return batch.out[layer].clone()
 
 
-@pytest.mark.parametrize("name", ["cfg2", "ragged40", "single_chunk400"])
+@pytest.mark.parametrize("name", ["cfg2", "ragged40", "single_chunk400", "odd_splits10",
+                                  "odd_splits11", "odd_splits13", "odd_splits22"])
 def test_two_phase_equals_fused_and_is_deterministic(torch_gpu, rope, name):
     spec = SMALL[name]()
     hw = wl.make_host_workload(spec)
     batch = host_batch(hw, rope)
+    if name.startswith("odd_splits"):
+        assert batch.splits == {10: 7, 11: 6, 13: 5, 22: 3}[spec.num_seqs]
     batch.append(0)
     a = _run_attn(batch)
     b = _run_attn(batch)
