@@ -103,8 +103,10 @@ int paged_kv_rope_table(double theta, int32_t max_pos, float* cos_out, float* si
  * n = context_lens[s] >= 1 (the length AFTER this append), the new token sits
  * at position pos = n-1:
  *   - the 32 heads of q[s] and the 8 heads of k_new[s] are rotated by the
- *     table row pos (pairs (i, i+32), i < 32), each result rounded once to
- *     BF16 with ties to even; q[s] is overwritten in place;
+ *     table row pos (pairs (i, i+32), i < 32: x_i c - x_{i+32} s and
+ *     x_{i+32} c + x_i s); each result is the FP64 value of that expression
+ *     (both products are exact in FP64) rounded once to BF16, ties to even;
+ *     q[s] is overwritten in place;
  *   - rotated K and unchanged V of KV head g go to page
  *     block_table[s*bt_stride + pos/16], slot pos%16.
  * Sequences with n <= 0 are skipped (nothing written).  A sequence whose

@@ -5,7 +5,8 @@
 Compiles csrc/kernels.hip (device code + launches) and csrc/api.cpp (the C
 ABI) into paged_kv_cache_172_amd/libpagedkv.so.  Packed FP32 instructions are
 disabled for device code (-target-feature -packed-fp32-ops): the kernels use
-plain FP32 and FP64 VALU, DPP, permlane swaps and v_mfma_f32_16x16x32_bf16.
+plain FP32 and FP64 VALU, DPP, permlane swaps, the BF16 pack conversion,
+v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16.
 """
 from __future__ import annotations
 

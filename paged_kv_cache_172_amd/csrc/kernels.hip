@@ -643,7 +643,7 @@ static_assert(kRotTasks <= 64, "one task per lane");
 // kFused = false: paged decode attention over the cache as it is (q already
 // rotated by the append).  kFused = true: the same, with the append of the
 // new token done in the same launch: q and the new K are rotated here (the
-// same FP64 rotation and rounding as append_kernel), q is used without being
+// same rotation and rounding as append_kernel, rope4), q is used without being
 // written back, the K/V row is written into its page by the workgroup of
 // outer chunk 0, and the attention reads the new token from registers.
 template <bool kFused>
