@@ -112,13 +112,15 @@ __device__ __forceinline__ uint32_t f64_to_bf16_normal(double y, bool& ok) {
 // One rotated element in FP32, u*c - v*s: p = v*s rounded and its exact
 // error e (an FMA); r = u*c - p rounded; y = r - e rounded.  Then
 // |y - (u c - v s)| <= ulp(r)/2 + ulp(y)/2 + 2^-150 (the last term if e
-// underflowed), at most 2 ulp(y) when |r| <= 2|y| and y is normal.  y then
+// underflowed; FP32 denormals are kept, as these kernels are compiled), at
+// most 2 ulp(y) when |r| <= 2|y| and y is normal.  y then
 // rounds to BF16 as the exact value (and its FP64 rounding) does when y lies
 // at least 3 FP32 ulps from every BF16 half-way point: its low 16 bits
 // outside 0x8000 +- 2 (points across a binade edge lie 2^15 ulps away or
 // more).  The caller folds the three conditions over its elements:
 //   margin: the minimum of (bits(y) << 16) + 0x80020000 is >= 5 << 16;
-//   slack:  the minimum of 2|y| - |r| is >= 0 (its sign is exact);
+//   slack:  the minimum of 2|y| - |r| is >= 0 (its sign is exact: both are
+//           on the 2^-149 grid, so a nonzero difference never rounds to 0);
 //   normal: every y is a normal number.
 struct RotCheck {
     uint32_t margin = 0xFFFFFFFFu;
