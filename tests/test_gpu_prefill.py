@@ -333,3 +333,34 @@ def test_rotation_rounding_edges(torch_gpu, orc, rope):
     one = Dev(torch_gpu, c, table)
     one.appends(c)
     assert torch_gpu.equal(one.pages, dev.pages) and torch_gpu.equal(one.q, dev.q)
+
+
+def test_prefill_strided_layouts(torch_gpu, orc, rope):
+    """Packed QKV rows ([T][3072]: q, then k, then v) and a [slot][head][dim]
+    page layout: the fill rotates q in place inside the packed rows, leaves
+    k and v as given, and writes the oracle's pool bits through the strides."""
+    torch = torch_gpu
+    c = make_case(716, [0, 5, 2000], [40, 27, 48])
+    ref_pages, ref_q = oracle_prefill(orc, c, rope)
+    d = torch.device("cuda")
+    T = int(c["cu"][-1])
+    P = c["pages"].shape[0]
+    # [page][K|V][slot 16][head 8][dim 64], NaN-poisoned like the default case
+    inter = torch.from_numpy(np.ascontiguousarray(c["pages"].transpose(0, 1, 3, 2, 4)).view(np.int16)).to(d)
+    half = 16 * 8 * 64
+    pool = pkv.make_pool(inter.data_ptr(), inter.data_ptr() + 2 * half, P, 2 * half, 64, 512)
+    qkv = torch.zeros((T, 3072), dtype=torch.int16, device=d)
+    qkv[:, :2048] = torch.from_numpy(c["q"].view(np.int16)).to(d)
+    qkv[:, 2048:2560] = torch.from_numpy(c["k"].view(np.int16)).to(d)
+    qkv[:, 2560:] = torch.from_numpy(c["v"].view(np.int16)).to(d)
+    kv_before = qkv[:, 2048:].clone()
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(d)
+    cos, sin = torch.from_numpy(rope[0]).to(d), torch.from_numpy(rope[1]).to(d)
+    pkv.paged_kv_prefill(pool, i32(c["bt"]), 128, i32(c["start"]), i32(c["cu"]), len(c["start"]), T,
+                         qkv, 3072, qkv[:, 2048:], 3072, qkv[:, 2560:], 3072, cos, sin,
+                         rope[0].shape[0])
+    torch.cuda.synchronize()
+    back = to_u16(inter).reshape(P, 2, 16, 8, 64).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(back, ref_pages), "pool differs from the oracle"
+    assert np.array_equal(to_u16(qkv[:, :2048].contiguous()), ref_q), "q differs from the oracle"
+    assert torch.equal(qkv[:, 2048:], kv_before), "k and v must be left as given"
