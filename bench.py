@@ -126,6 +126,55 @@ def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
     }
 
 
+def time_continuous_batching(torch, stream, rope, reps: int):
+    """The continuous-batching mix: 256 sequences x 16 layers, context lengths
+    log-uniform in 16..2,048, 16 of them opening a page this step (lazy page
+    step first).  The fused step per layer, with the batch in its given order
+    and ordered longest-first by the caller (the kernels' results do not
+    depend on the order; with 2,048 (sequence, KV head) workgroups, twice what
+    the GPU holds at once, the order sets the tail)."""
+    from paged_kv_cache_172_amd import pages as pg, workload as wl
+    from paged_kv_cache_172_amd.runner import DecodeBatch
+    spec = wl.config_spec(4)
+    pool = wl.make_device_pool(spec)
+    q0, k0, v0 = wl.draw_new_tokens(spec)
+    bt = spec.block_tables.copy()
+    if len(spec.crossers):
+        pg.lazy_page_step(bt, spec.ctx, pg.FreeList(spec.free_pages, spec.num_pages))
+    L = spec.num_layers
+    kv_layer = spec.kv_bytes_per_step() / L
+    res = {"workload": f"{spec.num_seqs} sequences x {L} layers, context log-uniform 16..2048 "
+                       f"(sum {int(spec.ctx.sum())} tokens per layer)",
+           "kv_bytes_per_layer": int(kv_layer)}
+    longest = np.argsort(-spec.ctx, kind="stable")
+    for name, perm in (("given_order", None), ("longest_first", longest)):
+        if perm is None:
+            args = (bt, spec.ctx, q0, k0, v0)
+        else:
+            args = (np.ascontiguousarray(bt[:, perm]), np.ascontiguousarray(spec.ctx[perm]),
+                    *(np.ascontiguousarray(x[:, perm]) for x in (q0, k0, v0)))
+        b = DecodeBatch(pool, *args, rope=rope, max_context_len=wl.MAX_CONTEXT)
+        for _ in range(PREWARM_STEPS // 4):
+            for layer in range(L):
+                b.append_attn(layer, stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            for layer in range(L):
+                b.append_attn(layer, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (reps * L) * 1e3
+        res[name] = {"us_per_layer": round(us, 2), "kv_gbps": round(kv_layer / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(kv_layer / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del b
+    del pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_prefix_sharing(torch, pkv, stream, reps: int):
     """64 sequences of 2,048 tokens whose first 1,024 tokens are one shared
     prompt, tables built by the native pager (one layer): live pages with and
@@ -353,6 +402,7 @@ def main():
 
     prefill = time_prefill(torch, pkv, stream, batch.rope_cos, batch.rope_sin, max(3, a.steps // 2))
     prefix = time_prefix_sharing(torch, pkv, stream, max(3, a.steps))
+    mix = time_continuous_batching(torch, stream, rope, max(3, a.steps // 2))
 
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
@@ -414,6 +464,7 @@ def main():
     }
     result["prefill_fill"] = prefill
     result["prefix_sharing"] = prefix
+    result["continuous_batching"] = mix
     if free_stats:
         result["free_list"] = free_stats
     if not a.no_cpu_baseline:

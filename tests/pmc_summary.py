@@ -2,7 +2,7 @@
 
     python -m tests.pmc_summary --fetch F.csv --write W.csv \
         --copy-fetch CF.csv --copy-write CW.csv --kernel attn_split_kernel<true> \
-        --splits 1 [--json out.json]
+        --splits 1 [--grid 131072] [--json out.json]
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel are averaged over
 its dispatches and scaled by what the same counters read for the 256 MiB
@@ -26,11 +26,14 @@ if ROOT not in sys.path:
 COPY_BYTES = 256 * 2 ** 20
 
 
-def counter_values(path: str, kernel_substr: str, counter: str):
+def counter_values(path: str, kernel_substr: str, counter: str, grid: int = 0):
+    """Values of one counter for the dispatches of a kernel (only those of
+    grid size `grid` work-items when it is nonzero)."""
     vals = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"] and \
+                    (not grid or int(r["Grid_Size"]) == grid):
                 vals.append(float(r["Counter_Value"]))
     return vals
 
@@ -52,10 +55,12 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--kernel", required=True)
     ap.add_argument("--splits", type=int, required=True)
+    ap.add_argument("--grid", type=int, default=0,
+                    help="only dispatches of this grid size in work-items (one workload)")
     ap.add_argument("--json")
     a = ap.parse_args()
-    fetch = counter_values(a.fetch, a.kernel, "FETCH_SIZE")
-    write = counter_values(a.write, a.kernel, "WRITE_SIZE")
+    fetch = counter_values(a.fetch, a.kernel, "FETCH_SIZE", a.grid)
+    write = counter_values(a.write, a.kernel, "WRITE_SIZE", a.grid)
     if not fetch or not write:
         sys.exit(f"no dispatches of {a.kernel!r} in the counter files")
     f_cal = calibration(a.copy_fetch, "FETCH_SIZE")
