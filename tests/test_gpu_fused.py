@@ -192,3 +192,28 @@ def test_fused_strided_layouts(torch_gpu, rope):
     back = inter.view(spec.num_pages, 2, 16, 8, 64).permute(0, 1, 3, 2, 4).contiguous()
     assert torch.equal(back, ref_pool.view(back.shape)), "pool differs from append"
     assert torch.equal(qkv, qkv_before), "the fused call must leave q, k and v as given"
+
+
+def test_fused_rotation_rounding_edges(torch_gpu):
+    """The fused kernel's rotation on the rounding edges (exact BF16 ties,
+    values beside a half-way point by less than an FP32 ulp, overflow,
+    subnormals, zeros, infinities, NaN; RoPE table rows built for them):
+    pool bits and output equal append + attention (NaN where NaN)."""
+    from tests.test_gpu_prefill import _edge_bf16, _edge_table
+    torch = torch_gpu
+    rng = np.random.Generator(np.random.PCG64(721))
+    lengths = list(range(1, 33))                 # new tokens at positions 0..31
+    spec = wl.make_spec(lengths, 1, seed=721)
+    hw = wl.make_host_workload(spec)
+    B = spec.num_seqs
+    hw.q[0] = _edge_bf16(rng, (B, 2048))
+    hw.k[0] = _edge_bf16(rng, (B, 512))
+    hw.v[0] = _edge_bf16(rng, (B, 512))
+    table = _edge_table(rng, 32)
+
+    def make():
+        return DecodeBatch(hw.pages, spec.block_tables, spec.ctx, hw.q, hw.k, hw.v, rope=table,
+                           max_context_len=32)
+    sep, fus = run_both(torch, make, 1)
+    assert same_bits(torch, fus.pool_pages, sep.pool_pages), "pool differs from append"
+    assert same_bits(torch, fus.out, sep.out), "output differs from append + attention"
