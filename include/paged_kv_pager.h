@@ -167,8 +167,14 @@ int paged_kv_pager_reserve(paged_kv_pager* pg, int64_t request_id, int32_t lengt
 /*
  * paged_kv_pager_reserve for the requests of one decode batch (ids[i] grows
  * to lengths[i]; its table row is tables + i*seq_stride), recording the batch
- * size for the statistics.  All lengths are checked before any page moves.
+ * size for the statistics.  All lengths, and the pages the whole batch
+ * needs, are checked before any page moves.  Copies are counted per physical
+ * page: a shared page held by r requests and written by w of them in this
+ * step costs min(w, r-1) copies (the last holder left writes in place), the
+ * same as reserving the requests one by one.
  * copy_src/copy_dst need room for n * num_layers pairs.
+ * Errors: those of reserve; EXHAUSTED (nothing changed) only if a broken
+ * invariant leaves fewer free pages than the batch needs.
  */
 int paged_kv_pager_decode_step(paged_kv_pager* pg, const int64_t* ids, const int32_t* lengths,
                                int32_t n, int32_t* tables, int64_t seq_stride,

@@ -146,19 +146,33 @@ struct paged_kv_pager {
         return PKV_OK;
     }
 
-    // Pages grow() would take: copies of shared pages the new tokens land
-    // in, plus new logical pages, in every layer.
-    int64_t pages_needed(const Request& r, int32_t length, int64_t* cow = nullptr) const {
-        int64_t c = 0;
-        if (cow) *cow = 0;
+    // New logical pages grow() would take for r, in every layer.
+    int64_t fresh_pages(const Request& r, int32_t length) const {
         if (length <= r.length) return 0;
         const int64_t held = (int64_t)r.pages[0].size();
-        const int64_t fresh = (pages_for(length) - std::min<int64_t>(held, pages_for(length))) * layers;
+        return (pages_for(length) - std::min<int64_t>(held, pages_for(length))) * layers;
+    }
+
+    // Adds to `writers` one count per shared page (refs > 1) that the new
+    // tokens of r land in.
+    void shared_writes(const Request& r, int32_t length,
+                       std::unordered_map<int32_t, int32_t>& writers) const {
+        if (length <= r.length) return;
+        const int64_t held = (int64_t)r.pages[0].size();
         for (int64_t j = r.length / kPageTokens; j < held && j * kPageTokens < length; ++j)
-            for (int32_t l = 0; l < layers; ++l)
-                if (refs[(size_t)r.pages[(size_t)l][(size_t)j]] > 1) ++c;
-        if (cow) *cow = c;
-        return fresh + c;
+            for (int32_t l = 0; l < layers; ++l) {
+                const int32_t p = r.pages[(size_t)l][(size_t)j];
+                if (refs[(size_t)p] > 1) ++writers[p];
+            }
+    }
+
+    // Copies grow() makes when the requests of one batch write into shared
+    // pages: a page held by r requests and written by w of them is copied
+    // min(w, r - 1) times, since the last holder left writes in place.
+    int64_t copies_needed(const std::unordered_map<int32_t, int32_t>& writers) const {
+        int64_t c = 0;
+        for (const auto& pw : writers) c += std::min<int64_t>(pw.second, refs[(size_t)pw.first] - 1);
+        return c;
     }
 
     // Grows r to `length` tokens (checked by check_reserve).  Pages that the
@@ -355,8 +369,10 @@ int paged_kv_pager_reserve(paged_kv_pager* pg, int64_t request_id, int32_t lengt
     if (st != PKV_OK) return st;
     // Admission keeps this from failing; the check only turns a broken
     // invariant into a status instead of a bad page id.
-    int64_t cow = 0;
-    if (pg->pages_needed(*r, length, &cow) > pg->fl.size()) return PKV_ERR_EXHAUSTED;
+    std::unordered_map<int32_t, int32_t> writers;
+    pg->shared_writes(*r, length, writers);
+    const int64_t cow = pg->copies_needed(writers);
+    if (pg->fresh_pages(*r, length) + cow > pg->fl.size()) return PKV_ERR_EXHAUSTED;
     if (cow > 0 && (!copy_src || !copy_dst)) return PKV_ERR_INVALID_ARG;   // copies to report
     int32_t nc = 0;
     pg->grow(*r, length, copy_src, copy_dst, &nc);
@@ -382,13 +398,18 @@ int paged_kv_pager_decode_step(paged_kv_pager* pg, const int64_t* ids, const int
         for (int32_t k = 0; k < i; ++k)
             if (ids[k] == ids[i]) return PKV_ERR_INVALID_ARG;   // one entry per request
     }
-    int64_t need = 0, cow = 0;
+    // Count before changing anything, so that an exhausted pool changes
+    // nothing.  Copies are counted per physical page over the whole batch:
+    // two holders of one shared page that both write in this step make one
+    // copy, not two.
+    int64_t fresh = 0;
+    std::unordered_map<int32_t, int32_t> writers;
     for (int32_t i = 0; i < n; ++i) {
-        int64_t c = 0;
-        need += pg->pages_needed(*rs[(size_t)i], lengths[i], &c);
-        cow += c;
+        fresh += pg->fresh_pages(*rs[(size_t)i], lengths[i]);
+        pg->shared_writes(*rs[(size_t)i], lengths[i], writers);
     }
-    if (need > pg->fl.size()) return PKV_ERR_EXHAUSTED;
+    const int64_t cow = pg->copies_needed(writers);
+    if (fresh + cow > pg->fl.size()) return PKV_ERR_EXHAUSTED;
     if (cow > 0 && (!copy_src || !copy_dst)) return PKV_ERR_INVALID_ARG;
     int32_t nc = 0;
     for (int32_t i = 0; i < n; ++i) {

@@ -136,6 +136,59 @@ def test_copy_on_write_of_a_shared_partial_page():
     assert pg.stats()["live_pages"] == 0 and pg.stats()["free_pages"] == 64
 
 
+def test_two_holders_writing_one_shared_page_in_a_batch_make_one_copy():
+    """A page two requests hold, written by both in one decode step, is
+    copied once: the first writer takes a copy, the second is then its only
+    holder and writes in place.  With exactly one free page the batch must
+    fit, as the same writes through two reserve() calls do."""
+    for batched in (True, False):
+        pg = pages.Pager(num_pages=2, num_layers=1)
+        a, _ = pg.submit(5, 11)
+        b, _ = pg.submit(5, 11)
+        assert pg.admit() == [a, b]               # credits: 1 page each
+        ta = np.full((1, 4), -1, np.int32)
+        tb = np.full((1, 4), -1, np.int32)
+        pg.reserve(a, 5, ta)
+        pg.share_prefix(a, b, 5, tb)
+        assert pg.stats()["free_pages"] == 1
+        if batched:
+            t = np.stack([ta, tb])
+            copies = pg.decode_step([a, b], [6, 6], t)
+            ta, tb = t[0], t[1]
+        else:
+            copies = pg.reserve(a, 6, ta) + pg.reserve(b, 6, tb)
+        assert len(copies) == 1
+        assert ta[0, 0] != tb[0, 0]
+        st = pg.stats()
+        assert st["free_pages"] == 0 and st["live_pages"] == 2
+        assert st["copies"] == 1 and st["shared_refs"] == 0
+
+
+@pytest.mark.parametrize("writers", [1, 2, 3])
+def test_copies_per_shared_page_in_a_batch(writers):
+    """A page held by 3 requests and written by w of them in one step costs
+    min(w, 2) copies, and the pool's 2 free pages cover every case."""
+    need = min(writers, 2)
+    pg2 = pages.Pager(num_pages=3, num_layers=1)   # credits: 1 page per request
+    ids = [pg2.submit(5, 11)[0] for _ in range(3)]
+    assert pg2.admit() == ids
+    t = np.full((3, 1, 4), -1, np.int32)
+    pg2.reserve(ids[0], 5, t[0])
+    pg2.share_prefix(ids[0], ids[1], 5, t[1])
+    pg2.share_prefix(ids[0], ids[2], 5, t[2])
+    assert pg2.stats()["free_pages"] == 2
+    chosen = ids[:writers]
+    tb = np.ascontiguousarray(t[:writers])
+    copies = pg2.decode_step(chosen, [6] * writers, tb)
+    assert len(copies) == need
+    st = pg2.stats()
+    assert st["copies"] == need and st["free_pages"] == 2 - need
+    assert st["live_pages"] == 1 + need
+    # every writer ends with a page only it holds, or the original page when
+    # it was the last holder left
+    assert len(set(tb[:, 0, 0].tolist())) == writers
+
+
 def test_share_of_whole_pages_needs_no_copy():
     pg = pages.Pager(num_pages=64, num_layers=L)
     a, _ = pg.submit(32, 10)
@@ -220,13 +273,17 @@ def test_admission_wait_is_measured():
     assert st["wait_total_us"] >= st["wait_max_us"]
 
 
-def test_random_run_never_runs_dry():
+@pytest.mark.parametrize("seed,P,share_p", [(820, 300, 0.1), (821, 120, 0.9)])
+def test_random_run_never_runs_dry(seed, P, share_p):
     """Seeded random traffic: submits, FIFO admission, decode growth, prefix
     sharing between fresh requests, early finishes.  After every step: free +
     live = pool, live <= credits held, the tables' references match the
-    pager's counts, and no reserve runs out of pages."""
-    rng = np.random.default_rng(820)
-    P, LL, W = 300, 3, 40
+    pager's counts, and no reserve runs out of pages.  The second run shares
+    almost every fresh request's prefix in a small pool, so that several
+    holders of one shared page write into it in the same decode step."""
+    rng = np.random.default_rng(seed)
+    LL, W = 3, 40
+    multi_writer_steps = 0
     pg = pages.Pager(num_pages=P, num_layers=LL, max_context=600)
     tables, length, budget, prompt = {}, {}, {}, {}
     waiting = []
@@ -246,12 +303,13 @@ def test_random_run_never_runs_dry():
             tables[rid] = np.full((LL, W), -1, np.int32)
             length[rid] = 0
         active = list(tables)
-        if active and rng.random() < 0.1:
-            # a fresh request takes another's prefix
-            fresh = [x for x in active if length[x] == 0]
-            holders = [x for x in active if length[x] > 0]
-            if fresh and holders:
-                dst, src = fresh[0], holders[int(rng.integers(len(holders)))]
+        if active and rng.random() < share_p:
+            # fresh requests take another's prefix
+            for dst in [x for x in active if length[x] == 0]:
+                holders = [x for x in active if length[x] > 0]
+                if not holders:
+                    break
+                src = holders[int(rng.integers(len(holders)))]
                 n = min(length[src], prompt[dst])
                 if n >= 1:
                     pg.share_prefix(src, dst, n, tables[dst])
@@ -259,6 +317,13 @@ def test_random_run_never_runs_dry():
         batch = [x for x in active if length[x] < budget[x]]
         if batch:
             lens = [min(budget[x], length[x] + int(rng.integers(1, 40))) for x in batch]
+            written = {}
+            for x, n in zip(batch, lens):
+                held = -(-length[x] // 16)
+                for j in range(length[x] // 16, min(held, -(-n // 16))):
+                    for p in tables[x][:, j].tolist():
+                        written[p] = written.get(p, 0) + 1
+            multi_writer_steps += any(c > 1 for c in written.values())
             tb = np.stack([tables[x] for x in batch])
             pg.decode_step(batch, lens, tb)      # must never raise PoolExhausted
             for x, t, n in zip(batch, tb, lens):
@@ -281,6 +346,8 @@ def test_random_run_never_runs_dry():
         assert len(refs) == st["live_pages"]
         assert sum(refs.values()) - len(refs) == st["shared_refs"]
     assert pg.stats()["admitted"] > 50 and pg.stats()["copies"] > 0
+    if share_p > 0.5:
+        assert multi_writer_steps >= 5, multi_writer_steps
 
 
 def test_lazy_page_step_is_all_or_nothing():
