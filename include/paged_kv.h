@@ -77,7 +77,10 @@ extern "C" {
  * Default layout: page = [K | V][8 heads][16 slots][64 dims] BF16 = 32 KiB,
  * i.e. page_stride 16384, head_stride 1024, slot_stride 64 and
  * v_pool = k_pool + 8192.  k_pool and v_pool: (device), 16-byte aligned;
- * the three strides must be positive multiples of 8 elements.
+ * the three strides must be positive multiples of 8 elements, slot_stride at
+ * least 64, and the 16 slots of one head must span less than 2^30 elements
+ * (15*slot_stride + 64 < 2^30); num_pages must fit in int32.  Pools outside
+ * these bounds are refused with INVALID_ARG (ALIGNMENT for the multiples).
  */
 typedef struct paged_kv_pool {
     uint16_t* k_pool;
@@ -211,10 +214,13 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
  * inputs; the context is cut into chunks (paged_decode_attn_num_splits)
  * whose partial results are merged with the log-sum-exp rule.  Rows with
  * n <= 0 are written as zeros; a length above max_context_len is clamped to
- * it.  Tokens at or past n, pages no table entry below ceil(n/16) names, and
- * table entries at or past ceil(n/16) are never read.  A table entry below
- * ceil(n/16) that is not a page in [0, num_pages) is not dereferenced; that
- * sequence's rows come out NaN.
+ * it.  K/V of tokens at or past n, and pages that no table entry below
+ * ceil(n/16) names, are never read.  Each row's first min(bt_stride, 128)
+ * table entries are loaded together when the row's work starts, whatever n
+ * is (so the table must be readable as [num_seqs][bt_stride]); entries at or
+ * past ceil(n/16) may hold any value, which is never used.  A table entry
+ * below ceil(n/16) that is not a page in [0, num_pages) is not dereferenced;
+ * that sequence's rows come out NaN.
  *   max_context_len  host-known upper bound of every context_lens[s] (drives the plan)
  *   q                (device) BF16 [num_seqs][q_stride], already rotated
  *   out              (device) FP32 [num_seqs][out_stride], >= 2048 per row

@@ -70,6 +70,11 @@ int check_pool(const paged_kv_pool* pool) {
         pool->slot_stride < pkv::kHeadDim)
         return PKV_ERR_INVALID_ARG;
     if (pool->num_pages > INT32_MAX) return PKV_ERR_INVALID_ARG;  // page ids are int32
+    // The attention reads each (page, KV head) tile through a buffer
+    // descriptor whose byte range and lane offsets are 32-bit: the 16 slots
+    // of a head must span less than 2^30 elements.
+    if ((pkv::kPageTokens - 1) * pool->slot_stride + pkv::kHeadDim >= ((int64_t)1 << 30))
+        return PKV_ERR_INVALID_ARG;
     if (!aligned16(pool->k_pool) || !aligned16(pool->v_pool)) return PKV_ERR_ALIGNMENT;
     if (pool->page_stride % 8 || pool->head_stride % 8 || pool->slot_stride % 8)
         return PKV_ERR_ALIGNMENT;

@@ -127,6 +127,10 @@ APPEND_CASES = [
     ({}, {"slot_stride": 32}, pkv.PKV_ERR_INVALID_ARG),
     ({}, {"head_stride": 1020}, pkv.PKV_ERR_ALIGNMENT),
     ({}, {"v_pool": FAKE + 6}, pkv.PKV_ERR_ALIGNMENT),
+    # 15 * slot_stride + 64 must stay below 2^30 elements (32-bit tile ranges)
+    ({}, {"slot_stride": 71582784}, pkv.PKV_ERR_INVALID_ARG),
+    ({}, {"slot_stride": 2 ** 40}, pkv.PKV_ERR_INVALID_ARG),
+    ({"q": FAKE + 2}, {"slot_stride": 71582776}, pkv.PKV_ERR_ALIGNMENT),   # largest accepted
 ]
 
 
@@ -176,6 +180,15 @@ ATTN_CASES = [
 @pytest.mark.parametrize("kw,want", ATTN_CASES)
 def test_attn_rejects(lib, fn, kw, want):
     assert _attn_status(fn, **kw) == want
+
+
+@pytest.mark.parametrize("fn", [pkv.paged_decode_attn, pkv.paged_decode_attn_split],
+                         ids=["attn", "split"])
+def test_attn_rejects_slot_stride_past_32bit_tiles(lib, fn):
+    """The attention's per-tile buffer ranges are 32-bit: a slot stride whose
+    16 slots span 2^30 elements or more is refused before any launch."""
+    assert _attn_status(fn, _pool(slot_stride=71582784)) == pkv.PKV_ERR_INVALID_ARG
+    assert _attn_status(fn, _pool(slot_stride=71582776), q=FAKE + 2) == pkv.PKV_ERR_ALIGNMENT
 
 
 def test_attn_zero_seqs_is_noop(lib):
