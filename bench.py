@@ -247,22 +247,42 @@ def measured_traffic(splits: int):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s: float):
+THREAD_CAP = 16      # a GPU machine's CPU share for one GPU
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pages, bt_all, ctx_all, q0, k0, v0, rope, budget_s: float,
+                 one_core_budget_s: float = 3.0, what: str = "step"):
     """Time the FP64 oracle (append + attention) on whole (layer, sequence)
-    units of this workload, reading a host copy of the pool: one unit on one
-    thread sizes the sample, then a bounded sample (about budget_s seconds of
-    CPU work, at most one full step) runs spread over the host threads."""
+    units of a workload, reading a host copy of its pool.
+
+    Two figures, both with the same plain single-threaded oracle calls:
+      - one core: units run one after another on one thread for about
+        one_core_budget_s seconds;
+      - N threads: a bounded sample (about budget_s seconds of CPU work, at
+        most every unit once) spread over min(host cores, THREAD_CAP)
+        threads, each unit one call.
+    The oracle writes each unit's new K/V row into the host pool (the same
+    bits the GPU wrote there), so repeated units do identical work."""
     import concurrent.futures
     import oracle
     from oracle import PoolView
 
     orc = oracle.default()
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    pages = batch.pool_pages.cpu().numpy().view(np.uint16)
+    host_cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(THREAD_CAP, host_cores))
     pool = PoolView.from_pages(pages)
-    bt_all = batch.block_tables.cpu().numpy()
-    ctx_all = batch.context_lens_host
-    L, B = spec.num_layers, spec.num_seqs
+    L, B = bt_all.shape[0], bt_all.shape[1]
     units = [(layer, s) for layer in range(L) for s in range(B)]
     np.random.default_rng(1720).shuffle(units)
 
@@ -276,10 +296,16 @@ def cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s: float):
         orc.attn(pool, bt, ctx, q, 0.125)
         return int(ctx[0])
 
+    # one core
     t0 = time.perf_counter()
-    run_unit(units[0])
-    one = time.perf_counter() - t0
-    n_units = int(min(len(units), max(threads, budget_s / max(one, 1e-4))))
+    done, kv1 = 0, 0
+    while done < len(units) and (done == 0 or time.perf_counter() - t0 < one_core_budget_s):
+        kv1 += run_unit(units[done]) * 2048
+        done += 1
+    one_wall = time.perf_counter() - t0
+    per_unit = one_wall / done
+    # N threads, bounded sample
+    n_units = int(min(len(units), max(threads, budget_s / max(per_unit, 1e-5))))
     sample = units[:n_units]
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
@@ -291,13 +317,103 @@ def cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s: float):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{len(sample)} of the {len(units)} (layer, sequence) units of one step, "
+        "sample": (f"{len(sample)} of the {len(units)} (layer, sequence) units of one {what}, "
                    f"each FP64 append + attention over its full context, on {threads} host "
-                   f"threads (~{one * len(sample):.0f} s of CPU work)"),
+                   f"threads (~{per_unit * len(sample):.2g} s of CPU work)"),
         "seq_layers_per_s": round(len(sample) / wall, 3),
-        "seconds": round(wall, 2),
-        "one_unit_one_thread_s": round(one, 4),
+        "seconds": round(wall, 3),
+        "host_cores": host_cores,
+        "thread_cap": THREAD_CAP,
+        "cpu_model": cpu_model(),
+        "one_core": {
+            "value": round(kv1 / one_wall / 1e9, 4),
+            "unit": "GB/s",
+            "seq_layers_per_s": round(done / one_wall, 3),
+            "units": done,
+            "seconds": round(one_wall, 3),
+        },
     }
+
+
+def batch_cpu_baseline(batch, spec, q0, k0, v0, rope, budget_s, what="step"):
+    pages = batch.pool_pages.cpu().numpy().view(np.uint16)
+    return cpu_baseline(pages, batch.block_tables.cpu().numpy(), batch.context_lens_host, q0, k0,
+                        v0, rope, budget_s, what=what)
+
+
+def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budget_s):
+    """Configs 1, 2 (latency of one layer's step; cache-resident, so not an
+    HBM roofline) and 5 (1,024 sequences x 2,048 tokens, one layer, 4 GiB of
+    KV; HBM-sized): the fused call, the two calls, and the attention alone,
+    each as the average of back-to-back launches between two HIP events on
+    the launch stream; with the oracle timed on the same workload."""
+    from paged_kv_cache_172_amd import workload as wl
+    from paged_kv_cache_172_amd.runner import DecodeBatch
+    spec = wl.config_spec(k)
+    if k == 5:
+        pool = wl.make_device_pool(spec)
+        q0, k0, v0 = wl.draw_new_tokens(spec)
+    else:
+        hw = wl.make_host_workload(spec)
+        pool, q0, k0, v0 = hw.pages, hw.q, hw.k, hw.v
+    b = DecodeBatch(pool, spec.block_tables, spec.ctx, q0, k0, v0, rope=rope,
+                    max_context_len=wl.MAX_CONTEXT)
+    del pool
+    L = spec.num_layers
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * L) * 1e3      # us per layer
+
+    def fused():
+        for layer in range(L):
+            b.append_attn(layer, stream)
+
+    def unfused():
+        for layer in range(L):
+            b.append(layer, stream)
+            b.attn(layer, stream)
+
+    def attn():
+        for layer in range(L):
+            b.attn(layer, stream)
+
+    us_f = timed(fused)
+    us_u = timed(unfused)
+    us_a = timed(attn)
+    kv_layer = spec.kv_bytes_per_step() / L
+    res = {
+        "workload": f"config {k}: {spec.name}",
+        "num_seqs": spec.num_seqs, "num_layers": L,
+        "kv_bytes_per_layer": int(kv_layer),
+        "splits": b.splits,
+        "fused_us_per_layer": round(us_f, 2),
+        "unfused_us_per_layer": round(us_u, 2),
+        "attn_us_per_layer": round(us_a, 2),
+        "kv_gbps_fused": round(kv_layer / (us_f * 1e-6) / 1e9, 1),
+        "kv_gbps_attn": round(kv_layer / (us_a * 1e-6) / 1e9, 1),
+    }
+    if k == 5:
+        alg = split_bytes_per_launch(spec.ctx, b.splits) + append_bytes_per_launch(spec.num_seqs)
+        res["frac_of_peak_fused"] = round(kv_layer / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        res["frac_of_peak_attn"] = round(kv_layer / (us_a * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        res["alg_frac_of_peak_fused"] = round(alg / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+    else:
+        res["note"] = "cache-resident: a latency, not an HBM roofline"
+    if cpu_budget_s is not None:
+        res["cpu_baseline"] = batch_cpu_baseline(b, spec, q0, k0, v0, rope, cpu_budget_s,
+                                                 what="layer")
+    del b
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -470,7 +586,18 @@ def main():
         result["free_list"] = free_stats
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(batch, spec, q0, k0, v0, rope, a.cpu_budget_s)
+        result["cpu_baseline"] = batch_cpu_baseline(batch, spec, q0, k0, v0, rope, a.cpu_budget_s)
+    del batch, pool
+    torch.cuda.empty_cache()
+    others = {}
+    for k in (1, 2, 5):
+        if k == a.config:
+            continue
+        log(f"[bench] config {k}")
+        others[f"config{k}"] = time_small_or_stress_config(
+            torch, k, stream, rope, reps=(200 if k < 5 else max(5, a.steps // 2)),
+            cpu_budget_s=None if a.no_cpu_baseline else (3.0 if k < 5 else 6.0))
+    result["other_configs"] = others
     print(json.dumps(result), flush=True)
 
 

@@ -2,6 +2,8 @@
 compare with the FP64 oracle on the same bytes."""
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
@@ -54,38 +56,32 @@ def to_u16(t) -> np.ndarray:
     return t.cpu().numpy().view(np.uint16)
 
 
-def gather_units(batch: DecodeBatch, units):
-    """Copy the pages of sampled (layer, seq) units back to the host as a
-    compact pool with remapped tables (the oracle's output does not depend on
-    where pages sit).  Returns (pages, bt [U][W], ctx [U], q [U][2048])."""
-    import torch
-    bt_all = batch.block_tables.cpu().numpy()
-    ctx_all = batch.context_lens_host
-    rows, ctx, qs, ids = [], [], [], []
-    for layer, s in units:
-        row = bt_all[layer, s]
-        n = int(ctx_all[s])
-        need = -(-n // 16) if n > 0 else 0
-        ids.extend(int(p) for p in row[:need])
-        rows.append((row, need))
-        ctx.append(n)
-        qs.append(to_u16(batch.q[layer, s]))
-    uniq = sorted(set(ids))
-    remap = {p: i for i, p in enumerate(uniq)}
-    idx = torch.tensor(uniq if uniq else [0], dtype=torch.int64, device=batch.device)
-    pages = to_u16(batch.pool_pages.index_select(0, idx)).copy()
-    bt = np.full((len(units), batch.bt_stride), -1, np.int32)
-    for u, (row, need) in enumerate(rows):
-        bt[u, :need] = [remap[int(p)] for p in row[:need]]
-    return pages, bt, np.asarray(ctx, np.int32), np.stack(qs)
+def host_threads() -> int:
+    """Threads for the oracle on the host: the cores this process may use,
+    at most 16 (a GPU machine's CPU share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def oracle_attn_units(batch: DecodeBatch, units, scale=0.125):
-    pages, bt, ctx, q = gather_units(batch, units)
-    return oracle.default().attn(PoolView.from_pages(np.ascontiguousarray(pages)), bt, ctx,
-                                 np.ascontiguousarray(q), scale)
+def oracle_attn_all(pages: np.ndarray, bt: np.ndarray, ctx: np.ndarray, q: np.ndarray,
+                    scale: float = 0.125) -> np.ndarray:
+    """The oracle's attention for every sequence of one layer, its rows split
+    into slices over the host threads (each slice is one plain
+    single-threaded oracle call; rows do not depend on each other).
+    pages: uint16 [P][2][8][16][64]; bt int32 [B][W]; ctx int32 [B]; q uint16
+    [B][2048].  Returns FP32 [B][2048]."""
+    orc = oracle.default()
+    pool = PoolView.from_pages(pages)
+    B = ctx.shape[0]
+    n = host_threads()
+    edges = np.linspace(0, B, min(n * 4, B) + 1).astype(int)
+    out = np.empty((B, q.shape[1]), np.float32)
 
+    def run(i):
+        a, b = edges[i], edges[i + 1]
+        if a < b:
+            out[a:b] = orc.attn(pool, np.ascontiguousarray(bt[a:b]), np.ascontiguousarray(ctx[a:b]),
+                                np.ascontiguousarray(q[a:b]), scale)
 
-def gpu_out_units(batch: DecodeBatch, units):
-    out = batch.out.cpu().numpy()
-    return np.stack([out[layer, s] for layer, s in units])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(run, range(len(edges) - 1)))
+    return out
