@@ -386,9 +386,15 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         for layer in range(L):
             b.attn(layer, stream)
 
+    def attn_two_phase():
+        for layer in range(L):
+            b.attn_split(layer, stream)
+            b.attn_combine(layer, stream)
+
     us_f = timed(fused)
     us_u = timed(unfused)
     us_a = timed(attn)
+    us_2 = timed(attn_two_phase)
     kv_layer = spec.kv_bytes_per_step() / L
     res = {
         "workload": f"config {k}: {spec.name}",
@@ -398,6 +404,7 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         "fused_us_per_layer": round(us_f, 2),
         "unfused_us_per_layer": round(us_u, 2),
         "attn_us_per_layer": round(us_a, 2),
+        "attn_split_then_combine_us_per_layer": round(us_2, 2),
         "kv_gbps_fused": round(kv_layer / (us_f * 1e-6) / 1e9, 1),
         "kv_gbps_attn": round(kv_layer / (us_a * 1e-6) / 1e9, 1),
     }
@@ -473,8 +480,7 @@ def main():
     def step_unfused():
         for layer in range(L):
             batch.append(layer, stream)
-            batch.attn_split(layer, stream)
-            batch.attn_combine(layer, stream)
+            batch.attn(layer, stream)
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -559,7 +565,7 @@ def main():
             "calls": "paged_kv_append + paged_decode_attn per layer",
         },
         "attn_only": {
-            "kernel": "attn_split_kernel<false>",
+            "kernel": "attn_split_kernel<false, false>",
             "kv_gbps": round(kv_layer / (split_avg * 1e-3) / 1e9, 2),
             "frac_of_peak": round(kv_layer / (split_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "alg_frac_of_peak": round(alg_split / (split_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -568,7 +574,7 @@ def main():
             "combine_launched": splits > 1,
         },
         "roofline": {
-            "kernel": "attn_split_kernel<true> (fused append + attention)",
+            "kernel": "attn_split_kernel<true, true> (fused append + attention)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -199,11 +199,29 @@ int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
 
 /*
  * Bytes of device workspace paged_decode_attn needs for this plan: 0 when
- * S == 1, else S * num_seqs * 32 * 66 * 4 (per workgroup partial and query
- * head: 64 accumulator values, a maximum and a sum, FP32).
- * Returns 0 for arguments outside the ranges above.
+ * S == 1, else 2048 + S * num_seqs * 32 * 66 * 4.  The first 2048 bytes are
+ * 512 int32 counters, one per (sequence, KV head) for up to 64 sequences
+ * (the plan only asks for S > 1 below 64 sequences); then come the partials,
+ * per workgroup and query head 64 accumulator values, a maximum and a sum,
+ * FP32.  Returns 0 for arguments outside the ranges above.
  */
 size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_len);
+
+/*
+ * Makes a workspace ready for use: zeroes its counter block (the first
+ * min(workspace_bytes, 2048) bytes), asynchronously on `stream`.  Call it
+ * once after allocating a workspace (zeroing the whole allocation instead
+ * does the same); paged_decode_attn and paged_kv_append_decode_attn leave
+ * the counters zero again when they finish, so a workspace serves any
+ * number of calls, of any num_seqs and max_context_len, without it.  A
+ * workspace whose counters are not zero makes those calls produce wrong
+ * output rows (they never wait, so nothing hangs).  The counter block is a
+ * plain fill; it is not meant for a captured graph (make the workspace
+ * ready before capture).
+ *   workspace  (device) 16-byte aligned, or NULL when workspace_bytes is 0
+ * Errors: INVALID_ARG (NULL with workspace_bytes > 0), ALIGNMENT, HIP.
+ */
+int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Paged decode attention ([HN-attn], [HN-batch], [TV-decode]).  For each
@@ -212,7 +230,11 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
  * over the logical token order t, where token t is read from page
  * block_table[s*bt_stride + t/16], slot t%16.  FP32 online softmax over BF16
  * inputs; the context is cut into chunks (paged_decode_attn_num_splits)
- * whose partial results are merged with the log-sum-exp rule.  Rows with
+ * whose partial results are merged with the log-sum-exp rule.  One launch:
+ * when S > 1, the last of a (sequence, KV head)'s S workgroups to finish
+ * merges their partials into the output (the combine phase's arithmetic,
+ * in the same order, so the result equals split + combine bit for bit),
+ * counting finished workgroups in the workspace's counters.  Rows with
  * n <= 0 are written as zeros; a length above max_context_len is clamped to
  * it.  K/V of tokens at or past n, and pages that no table entry below
  * ceil(n/16) names, are never read.  Each row's first min(bt_stride, 128)
@@ -225,8 +247,10 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
  *   q                (device) BF16 [num_seqs][q_stride], already rotated
  *   out              (device) FP32 [num_seqs][out_stride], >= 2048 per row
  *   workspace        (device) >= paged_decode_attn_workspace_size() bytes,
- *                    16-byte aligned; may be NULL when that size is 0.
- *                    Calls running concurrently need separate workspaces.
+ *                    16-byte aligned, made ready once with
+ *                    paged_decode_attn_workspace_init (counters zero); may
+ *                    be NULL when that size is 0.  Calls running
+ *                    concurrently need separate workspaces.
  * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
  * [1, min(2048, 16*bt_stride)], non-finite scale, a stride below its row
  * width), ALIGNMENT (out_stride must be a multiple of 4), WORKSPACE, HIP.
@@ -240,13 +264,15 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
 /*
  * The two phases of paged_decode_attn as separate calls, for callers that
  * time or schedule them apart.  Enqueuing paged_decode_attn_split then
- * paged_decode_attn_combine on one stream with the same arguments is exactly
- * paged_decode_attn.  The split phase streams the pages and writes one
- * partial (maximum, sum, accumulator) per workgroup into the workspace -- or,
- * when S == 1, the final rows into out.  The combine phase merges the
- * partials into out; when S == 1 it enqueues nothing.  The split phase takes
- * the arguments, checks and errors of paged_decode_attn; the combine phase
- * checks its own arguments the same way (INVALID_ARG, ALIGNMENT, WORKSPACE).
+ * paged_decode_attn_combine on one stream with the same arguments gives
+ * exactly paged_decode_attn's output bits.  The split phase streams the
+ * pages and writes one partial (maximum, sum, accumulator) per workgroup
+ * into the workspace -- or, when S == 1, the final rows into out; it does
+ * not use the counters.  The combine phase merges the partials into out in
+ * a launch of its own; when S == 1 it enqueues nothing.  The split phase
+ * takes the arguments, checks and errors of paged_decode_attn; the combine
+ * phase checks its own arguments the same way (INVALID_ARG, ALIGNMENT,
+ * WORKSPACE).
  */
 int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
                             int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,

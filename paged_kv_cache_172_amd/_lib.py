@@ -29,6 +29,7 @@ EXPORTED = (
     "paged_kv_append",
     "paged_decode_attn_num_splits",
     "paged_decode_attn_workspace_size",
+    "paged_decode_attn_workspace_init",
     "paged_decode_attn",
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
@@ -117,6 +118,7 @@ def load(path: str = LIB_PATH):
                             ctypes.c_int),
         "paged_decode_attn_num_splits": ([i32, i32], i32),
         "paged_decode_attn_workspace_size": ([i32, i32], ctypes.c_size_t),
+        "paged_decode_attn_workspace_init": ([P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, f32, P, i64, P, ctypes.c_size_t,
                                P], ctypes.c_int),
         "paged_decode_attn_split": ([PP, P, i64, P, i32, i32, P, i64, f32, P, i64, P,
@@ -217,6 +219,12 @@ def paged_decode_attn_num_splits(num_seqs: int, max_context_len: int) -> int:
 
 def paged_decode_attn_workspace_size(num_seqs: int, max_context_len: int) -> int:
     return int(load().paged_decode_attn_workspace_size(int(num_seqs), int(max_context_len)))
+
+
+def paged_decode_attn_workspace_init(workspace, workspace_bytes, stream=None) -> None:
+    _check(load().paged_decode_attn_workspace_init(_p(workspace), int(workspace_bytes),
+                                                   _stream(stream)),
+           "paged_decode_attn_workspace_init")
 
 
 def _attn_args(pool, block_table, bt_stride, context_lens, num_seqs, max_context_len, q,

@@ -20,13 +20,10 @@ namespace pkv {
 // of a 256-CU part) so that small batches still fill the chip, and never cuts
 // chunks of a full-length context below kMinPagesPerSplit pages.  It depends
 // only on (num_seqs, max_context_len).
-#ifndef PKV_TARGET_WAVES
-#define PKV_TARGET_WAVES 2048
-#endif
 #ifndef PKV_MIN_PAGES_PER_SPLIT
 #define PKV_MIN_PAGES_PER_SPLIT 4
 #endif
-constexpr int64_t kTargetWaves = PKV_TARGET_WAVES;
+constexpr int64_t kTargetWaves = kPlanTargetWaves;
 constexpr int32_t kMinPagesPerSplit = PKV_MIN_PAGES_PER_SPLIT;
 
 static bool plan_args_ok(int32_t num_seqs, int32_t max_context_len) {
@@ -40,14 +37,18 @@ Plan make_plan(int32_t num_seqs, int32_t max_context_len) {
     const int64_t s_cap = max_pages / ((int64_t)kChunkWaves * kMinPagesPerSplit);
     if (s > s_cap) s = s_cap;
     if (s > kMaxSplits) s = kMaxSplits;
+    if (num_seqs >= kMergeSeqs) s = 1;   // already implied; the merge counters rely on it
     if (s < 1) s = 1;
     return Plan{(int32_t)s};
 }
 
+// Workspace when S > 1: [counters: kCounterBytes][acc [B][32][S][64] FP32]
+// [(max, sum) [B][32][S] float2].
 size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len) {
     const Plan plan = make_plan(num_seqs, max_context_len);
     if (plan.splits <= 1) return 0;
-    return (size_t)plan.splits * (size_t)num_seqs * kQHeads * kPartialFloats * sizeof(float);
+    return kCounterBytes +
+           (size_t)plan.splits * (size_t)num_seqs * kQHeads * kPartialFloats * sizeof(float);
 }
 
 }  // namespace pkv
@@ -99,6 +100,17 @@ int check_append(const paged_kv_pool* pool, const int32_t* block_table, int64_t 
         !aligned16(rope_sin) || q_stride % 8 || k_stride % 8 || v_stride % 8)
         return PKV_ERR_ALIGNMENT;
     return PKV_OK;
+}
+
+// Points the partial and counter arrays of p (plan and num_seqs set) into a
+// workspace laid out as workspace_bytes() describes.
+void set_workspace(pkv::AttnParams& p, void* workspace) {
+    char* base = static_cast<char*>(workspace);
+    const size_t acc_bytes =
+        (size_t)p.plan.splits * p.num_seqs * pkv::kQHeads * pkv::kHeadDim * sizeof(float);
+    p.ws_cnt = reinterpret_cast<int32_t*>(base);
+    p.ws_acc = reinterpret_cast<float*>(base + pkv::kCounterBytes);
+    p.ws_ml = reinterpret_cast<float2*>(base + pkv::kCounterBytes + acc_bytes);
 }
 
 struct AttnCheck {
@@ -161,12 +173,7 @@ AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int6
     p.plan = pkv::make_plan(num_seqs, max_context_len);
     p.out = out;
     p.out_stride = out_stride;
-    if (need > 0) {
-        const size_t acc_bytes =
-            (size_t)p.plan.splits * num_seqs * pkv::kQHeads * pkv::kHeadDim * sizeof(float);
-        p.ws_acc = static_cast<float*>(workspace);
-        p.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + acc_bytes);
-    }
+    if (need > 0) set_workspace(p, workspace);
     r.status = PKV_OK;
     return r;
 }
@@ -294,6 +301,14 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
     return pkv::workspace_bytes(num_seqs, max_context_len);
 }
 
+int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace_bytes == 0) return PKV_OK;
+    if (!workspace) return PKV_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return PKV_ERR_ALIGNMENT;
+    const size_t n = workspace_bytes < pkv::kCounterBytes ? workspace_bytes : pkv::kCounterBytes;
+    return hip_status(hipMemsetAsync(workspace, 0, n, static_cast<hipStream_t>(stream)));
+}
+
 int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
                             int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, const uint16_t* q, int64_t q_stride,
@@ -303,7 +318,7 @@ int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_tabl
                              max_context_len, q, q_stride, scale, out, out_stride, workspace,
                              workspace_bytes);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;
-    return hip_status(pkv::launch_attn_split(c.params, static_cast<hipStream_t>(stream)));
+    return hip_status(pkv::launch_attn_split(c.params, false, static_cast<hipStream_t>(stream)));
 }
 
 int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
@@ -327,10 +342,7 @@ int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
     p.plan = plan;
     p.out = out;
     p.out_stride = out_stride;
-    const size_t acc_bytes =
-        (size_t)plan.splits * num_seqs * pkv::kQHeads * pkv::kHeadDim * sizeof(float);
-    p.ws_acc = static_cast<float*>(const_cast<void*>(workspace));
-    p.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(const_cast<void*>(workspace)) + acc_bytes);
+    set_workspace(p, const_cast<void*>(workspace));
     return hip_status(pkv::launch_attn_combine(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -342,10 +354,7 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
                              max_context_len, q, q_stride, scale, out, out_stride, workspace,
                              workspace_bytes);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int st = hip_status(pkv::launch_attn_split(c.params, s));
-    if (st != PKV_OK || c.params.plan.splits <= 1) return st;
-    return hip_status(pkv::launch_attn_combine(c.params, s));
+    return hip_status(pkv::launch_attn_split(c.params, true, static_cast<hipStream_t>(stream)));
 }
 
 int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_table,
@@ -372,10 +381,7 @@ int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_
     p.rope_cos = rope_cos;
     p.rope_sin = rope_sin;
     p.max_pos = max_pos;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int ls = hip_status(pkv::launch_append_attn_split(p, s));
-    if (ls != PKV_OK || p.plan.splits <= 1) return ls;
-    return hip_status(pkv::launch_attn_combine(p, s));
+    return hip_status(pkv::launch_append_attn_split(p, static_cast<hipStream_t>(stream)));
 }
 
 const char* paged_kv_status_string(int status) {

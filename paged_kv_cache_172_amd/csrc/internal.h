@@ -79,6 +79,17 @@ struct Plan {
     int32_t splits;
 };
 
+// The plan asks for S > 1 only while num_seqs * 8 * kChunkWaves wavefronts
+// fall short of its target of kPlanTargetWaves, i.e. for fewer than
+// kMergeSeqs sequences.  The in-kernel merge of those S partials counts the
+// finished workgroups of each (sequence, KV head) in a fixed block of
+// kMergeSeqs * 8 int32 counters at the start of the workspace, whatever
+// num_seqs is, so that every call finds its counters at the same place.
+constexpr int64_t kPlanTargetWaves = 2048;
+constexpr int kMergeSeqs = (int)(kPlanTargetWaves / (kKVHeads * kChunkWaves));
+constexpr size_t kCounterBytes = (size_t)kMergeSeqs * kKVHeads * sizeof(int32_t);
+static_assert(kCounterBytes % 256 == 0, "partials start 256-byte aligned");
+
 struct AttnParams {
     const uint16_t* k_pool;
     const uint16_t* v_pool;
@@ -96,6 +107,7 @@ struct AttnParams {
     int64_t out_stride;
     float* ws_acc;     // [num_seqs][32][S][64]
     float2* ws_ml;     // [num_seqs][32][S] (maximum in base-2 units, sum)
+    int32_t* ws_cnt;   // [kMergeSeqs][8] finished workgroups per (sequence, KV head)
     // Fused append only (launch_append_attn_split): the same pool, writable,
     // the new token's k/v rows and the RoPE table.
     uint16_t* k_pool_w;
@@ -115,7 +127,9 @@ size_t workspace_bytes(int32_t num_seqs, int32_t max_context_len);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_copy_pages(const CopyParams& p, hipStream_t stream);
-hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream);
+// merge: when S > 1, the last workgroup of each (sequence, KV head) to
+// finish merges the S partials into out (no combine launch needed).
+hipError_t launch_attn_split(const AttnParams& p, bool merge, hipStream_t stream);
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);
 

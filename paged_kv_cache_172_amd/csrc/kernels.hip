@@ -633,6 +633,65 @@ __device__ __forceinline__ void ring_fill(PageRing& ring, int pb, Issue& issue) 
     }
 }
 
+// The log-sum-exp merge of the S outer-chunk partials of one query head:
+// with M = max_c m_c (base 2), out = sum_c 2^(m_c - M) acc_c / sum_c
+// 2^(m_c - M) l_c; an empty chunk (m_c = -inf) weighs 0.  The partials
+// arrive in kMaxSplits slots whose slots past S hold a reread partial; their
+// terms are selected exact zeros (never a product with the reread values,
+// which may be NaN), so the sums are those over the S.  The separate combine
+// kernel and the in-kernel merge both use these two steps, in the same
+// order, so the two paths give the same bits.
+struct MergeWeights {
+    float w[kMaxSplits];
+    float inv;   // 1 / sum of the weighted sums (0 when that sum is 0)
+};
+__device__ __forceinline__ MergeWeights merge_weights(const float2 (&ml)[kMaxSplits], int S) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) M = fmaxf(M, c < S ? ml[c].x : -INFINITY);
+    MergeWeights r;
+    float L = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) {
+        const bool in = c < S && ml[c].x != -INFINITY;
+        r.w[c] = in ? exp2_fast(ml[c].x - M) : 0.0f;
+        L = fmaf(r.w[c], c < S ? ml[c].y : 0.0f, L);
+    }
+    r.inv = L == 0.0f ? 0.0f : 1.0f / L;
+    return r;
+}
+__device__ __forceinline__ float merge_dim(const MergeWeights& mw, const float (&x)[kMaxSplits], int S) {
+    float a = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) a = fmaf(mw.w[c], c < S ? x[c] : 0.0f, a);
+    return a * mw.inv;
+}
+
+// Partials are exchanged between workgroups that may run on different XCDs,
+// whose L2 caches are not coherent with each other: they are written and
+// read with device-scope (agent) accesses, which the gfx950 memory model
+// makes coherent across the XCDs (write-through stores, loads that do not
+// take another XCD's stale line), so no L2 write-back or invalidation of
+// the whole cache is needed.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent(const float2* p) {
+    return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)),
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// Waits until this wave's stores have completed (on gfx9 the vector memory
+// counter covers stores), and keeps the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Row tasks of the fused append: 6 rows (query heads 4g..4g+3 and the new
 // K of head g, rotated; the new V of head g, copied) x 8 groups of 4 pairs
 // (dims i0..i0+3 and i0+32..i0+35).  Every wave runs all 48 in its lanes
@@ -648,7 +707,13 @@ static_assert(kRotTasks <= 64, "one task per lane");
 // same rotation and rounding as append_kernel, rope4), q is used without being
 // written back, the K/V row is written into its page by the workgroup of
 // outer chunk 0, and the attention reads the new token from registers.
-template <bool kFused>
+//
+// kMerge (S > 1 only): after writing its partials, each workgroup counts
+// itself in its (sequence, KV head)'s counter; the one that finds the other
+// S - 1 already counted merges the S partials into the output row (the
+// combine kernel's arithmetic, in the same order) and sets the counter back
+// to 0 for the next call.  No workgroup waits for another.
+template <bool kFused, bool kMerge>
 __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
 void attn_split_kernel(AttnParams p) {
     // Partials of the workgroup's 4 waves: [wave][head][64 dims] and (max, sum).
@@ -659,6 +724,7 @@ void attn_split_kernel(AttnParams p) {
     // Each wave's current page: V (and, fused, K) rows of its 16 tokens.
     __shared__ __align__(16) uint16_t lds_vt[kChunkWaves][kPageTokens * kTileRow];
     __shared__ __align__(16) uint16_t lds_kt[kFused ? kChunkWaves : 1][kPageTokens * kTileRow];
+    __shared__ int lds_last;   // kMerge: this workgroup is the last of its (sequence, KV head)
 
     const int lane = threadIdx.x & 63;
     const int w = uniform((int)(threadIdx.x >> 6));
@@ -856,17 +922,47 @@ void attn_split_kernel(AttnParams p) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), tile_rsrc(ob, kHeadDim * 4), lane * 4, 0,
                                               kStoreNonTemporal);
     } else {
-        const int64_t slot_idx = ((int64_t)s * kQHeads + h) * p.plan.splits + ci;
-        p.ws_acc[slot_idx * kHeadDim + lane] = o;
-        if (lane == 0) p.ws_ml[slot_idx] = make_float2(Mx, L);
+        const int S = p.plan.splits;
+        const int64_t slot_idx = ((int64_t)s * kQHeads + h) * S + ci;
+        store_agent(&p.ws_acc[slot_idx * kHeadDim + lane], o);
+        if (lane == 0) store_agent(&p.ws_ml[slot_idx], make_float2(Mx, L));
+        if constexpr (kMerge) {
+            // Count this workgroup once all 4 waves' partials are stored.
+            wait_stores();
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int done = __hip_atomic_fetch_add(&p.ws_cnt[s * kKVHeads + g], 1, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+                lds_last = done == S - 1;
+            }
+            __syncthreads();
+            if (lds_last) {
+                // Wave w merges query head h = 4g + w; lane = output dim.
+                const int64_t base = ((int64_t)s * kQHeads + h) * S;
+                float2 ml[kMaxSplits];
+                float x[kMaxSplits];
+#pragma unroll
+                for (int c = 0; c < kMaxSplits; ++c) {
+                    const int64_t slot = base + (c < S ? c : S - 1);
+                    ml[c] = load_agent(&p.ws_ml[slot]);
+                    x[c] = load_agent(&p.ws_acc[slot * kHeadDim + lane]);
+                }
+                const float ov = merge_dim(merge_weights(ml, S), x, S);
+                const char* ob = reinterpret_cast<const char*>(p.out + (int64_t)s * p.out_stride + h * kHeadDim);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), tile_rsrc(ob, kHeadDim * 4), lane * 4,
+                                                      0, kStoreNonTemporal);
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&p.ws_cnt[s * kKVHeads + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
 // One thread per (sequence, query head, 4 output dims): merges the S
-// outer-chunk partials with the log-sum-exp rule (empty ones weigh 0).  All
-// S (max, sum) pairs and accumulator quads are requested at once (an index
-// past S rereads the last partial and is then ignored), so the thread waits
-// for one round trip, not one per partial.
+// outer-chunk partials with the log-sum-exp rule (merge_weights, merge_dim).
+// All S (max, sum) pairs and accumulator quads are requested at once (an
+// index past S rereads the last partial and is then ignored), so the thread
+// waits for one round trip, not one per partial.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int d4 = (int)(tid & 15);
@@ -883,28 +979,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
         ml[c] = p.ws_ml[slot];
         v[c] = *reinterpret_cast<const float4*>(p.ws_acc + slot * kHeadDim + d4 * 4);
     }
-    // Past S every term is an exact 0 (selected, never a product with a
-    // reread partial, which may be NaN), so the sums are those over the S.
-    float M = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < kMaxSplits; ++c) M = fmaxf(M, c < S ? ml[c].x : -INFINITY);
-    float L = 0.0f;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    const MergeWeights mw = merge_weights(ml, S);
+    float xs[4][kMaxSplits];
 #pragma unroll
     for (int c = 0; c < kMaxSplits; ++c) {
-        const bool in = c < S && ml[c].x != -INFINITY;
-        const float w = in ? exp2_fast(ml[c].x - M) : 0.0f;
-        const float l = c < S ? ml[c].y : 0.0f;
-        const float4 x = c < S ? v[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        L = fmaf(w, l, L);
-        a.x = fmaf(w, x.x, a.x);
-        a.y = fmaf(w, x.y, a.y);
-        a.z = fmaf(w, x.z, a.z);
-        a.w = fmaf(w, x.w, a.w);
+        xs[0][c] = v[c].x;
+        xs[1][c] = v[c].y;
+        xs[2][c] = v[c].z;
+        xs[3][c] = v[c].w;
     }
-    const float inv = L == 0.0f ? 0.0f : 1.0f / L;
     *reinterpret_cast<float4*>(p.out + s * p.out_stride + h * kHeadDim + d4 * 4) =
-        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+        make_float4(merge_dim(mw, xs[0], S), merge_dim(mw, xs[1], S), merge_dim(mw, xs[2], S),
+                    merge_dim(mw, xs[3], S));
 }
 
 }  // namespace
@@ -929,16 +1015,23 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_attn_split(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_split(const AttnParams& p, bool merge, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
-    hipLaunchKernelGGL(attn_split_kernel<false>, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
-                       stream, p);
+    if (merge && p.plan.splits > 1) {
+        if (p.num_seqs > kMergeSeqs) return hipErrorInvalidValue;   // the plan never asks for it
+        hipLaunchKernelGGL((attn_split_kernel<false, true>), dim3((unsigned)blocks), dim3(kChunkWaves * 64),
+                           0, stream, p);
+    } else {
+        hipLaunchKernelGGL((attn_split_kernel<false, false>), dim3((unsigned)blocks), dim3(kChunkWaves * 64),
+                           0, stream, p);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream) {
     const int64_t blocks = (int64_t)p.num_seqs * kKVHeads * p.plan.splits;
-    hipLaunchKernelGGL(attn_split_kernel<true>, dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
+    if (p.plan.splits > 1 && p.num_seqs > kMergeSeqs) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_split_kernel<true, true>), dim3((unsigned)blocks), dim3(kChunkWaves * 64), 0,
                        stream, p);
     return hipGetLastError();
 }

@@ -65,6 +65,8 @@ class DecodeBatch:
                                device=self.device)
         self.ws_bytes = _lib.paged_decode_attn_workspace_size(self.num_seqs, self.max_context_len)
         self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=self.device)
+        _lib.paged_decode_attn_workspace_init(self.workspace, self.ws_bytes,
+                                              torch.cuda.current_stream(self.device))
         base = self.pool_pages.data_ptr()
         self.pool = _lib.make_pool(base, base + HALF_PAGE * 2, P, PAGE_ELEMS, 16 * 64, 64)
 

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -71,7 +71,7 @@ def test_plan_properties(lib, B, ctx):
     if S > 1:
         assert 4 * S * 4 <= pages
     ws = pkv.paged_decode_attn_workspace_size(B, ctx)
-    assert ws == (0 if S == 1 else S * B * 32 * 66 * 4)
+    assert ws == (0 if S == 1 else 2048 + S * B * 32 * 66 * 4)
 
 
 def test_plan_fills_the_chip_for_small_batches(lib):
@@ -214,6 +214,18 @@ def test_combine_rejects(lib):
     # a single-chunk plan has nothing to merge: returns OK without launching
     assert pkv.paged_decode_attn_num_splits(4096, 64) == 1
     assert st(num_seqs=4096, max_context_len=64, workspace=None) == pkv.PKV_OK
+
+
+def test_workspace_init_rejects(lib):
+    def st(ws, n):
+        try:
+            pkv.paged_decode_attn_workspace_init(ws, n)
+        except pkv.PagedKVError as e:
+            return e.status
+        return pkv.PKV_OK
+    assert st(None, 0) == pkv.PKV_OK            # nothing to make ready
+    assert st(None, 4096) == pkv.PKV_ERR_INVALID_ARG
+    assert st(FAKE + 4, 4096) == pkv.PKV_ERR_ALIGNMENT
 
 
 def test_status_strings(lib):

@@ -153,7 +153,7 @@ def test_fused_strided_layouts(torch_gpu, rope):
     ctx = torch.from_numpy(spec.ctx).to(dev)
     out = torch.zeros((B, 2056), dtype=torch.float32, device=dev)   # padded rows
     ws_bytes = pkv.paged_decode_attn_workspace_size(B, base.max_context_len)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     say(f"fused strided layouts: B={B} ctx={spec.ctx.tolist()}")
     pkv.paged_kv_append_decode_attn(pool, bt, 128, ctx, B, base.max_context_len, qkv, 3072,
                                     qkv[:, 2048:], 3072, qkv[:, 2560:], 3072, base.rope_cos,

@@ -168,6 +168,55 @@ def test_two_phase_equals_fused_and_is_deterministic(torch_gpu, rope, name):
     assert torch_gpu.equal(a, c), "split + combine differs from the fused call"
 
 
+def _attn_into(batch, layer, out, ws, ws_bytes, q_unrotated=None):
+    """One paged_decode_attn call of `batch`'s layer into `out` with the
+    given workspace; with q_unrotated, the fused call instead (which rotates
+    that q and rewrites the new token's K/V row with the same bits)."""
+    if q_unrotated is not None:
+        pkv.paged_kv_append_decode_attn(
+            batch.pool, batch.block_tables[layer], batch.bt_stride, batch.context_lens,
+            batch.num_seqs, batch.max_context_len, q_unrotated[layer], 2048, batch.k[layer], 512,
+            batch.v[layer], 512, batch.rope_cos, batch.rope_sin, batch.max_pos, batch.scale, out,
+            2048, ws, ws_bytes)
+    else:
+        pkv.paged_decode_attn(batch.pool, batch.block_tables[layer], batch.bt_stride,
+                              batch.context_lens, batch.num_seqs, batch.max_context_len,
+                              batch.q[layer], 2048, batch.scale, out, 2048, ws, ws_bytes)
+
+
+def test_in_kernel_merge_is_stable_and_leaves_counters_zero(torch_gpu, rope):
+    """The one-call attention merges the S partials inside the split launch
+    (the last workgroup of each (sequence, KV head) to finish).  64 calls
+    back to back on one workspace, plain and fused alternately, each into
+    its own output rows, all equal split + combine bit for bit; one
+    workspace serves batches of other sizes and split counts in turn; after
+    every call the counter block is zero again."""
+    torch = torch_gpu
+    names = ["cfg2", "odd_splits22", "odd_splits10", "short_batch", "odd_splits13"]
+    batches, q_raw = [], []
+    for name in names:
+        hw = wl.make_host_workload(SMALL[name]())
+        b = host_batch(hw, rope)
+        q_raw.append(b.q.clone())
+        b.append(0)                    # q rotated, new token written: the fused calls redo it
+        batches.append(b)
+    need = max(b.ws_bytes for b in batches)
+    ws = torch.zeros(need, dtype=torch.uint8, device=batches[0].device)
+    say(f"in-kernel merge: splits {[b.splits for b in batches]}, shared workspace {need} B")
+    for name, b, q0 in zip(names, batches, q_raw):
+        ref = _run_attn(b, two_phase=True)
+        if b.splits > 1:
+            reps = 64 if name == "cfg2" else 8
+            outs = torch.full((reps, b.num_seqs, 2048), float("nan"), device=b.device)
+            for r in range(reps):
+                _attn_into(b, 0, outs[r], ws, need, q_unrotated=q0 if r % 2 else None)
+            torch.cuda.synchronize()
+            for r in range(reps):
+                assert torch.equal(outs[r].view(torch.int32), ref.view(torch.int32)), (name, r)
+            counters = ws[:2048].view(torch.int32)
+            assert not counters.any(), (name, counters.nonzero().flatten().tolist()[:8])
+
+
 def test_page_permutation_is_bitwise_invariant(torch_gpu, rope):
     spec = SMALL["ragged40"]()
     hw = wl.make_host_workload(spec)
@@ -252,7 +301,7 @@ def test_strided_layouts(torch_gpu, orc, rope):
     ctx = torch.from_numpy(spec.ctx).to(dev)
     out = torch.zeros((B, 2056), dtype=torch.float32, device=dev)   # padded rows
     ws_bytes = pkv.paged_decode_attn_workspace_size(B, 2048)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     pkv.paged_kv_append(pool, bt, 128, ctx, B, qkv, 3072, qkv[:, 2048:], 3072, qkv[:, 2560:], 3072,
                         base.rope_cos, base.rope_sin, 2048)
     pkv.paged_decode_attn(pool, bt, 128, ctx, B, 2048, qkv, 3072, 0.125, out, 2056, ws, ws_bytes)

@@ -73,7 +73,7 @@ class Layout:
         B = len(ctx)
         out = self.torch.zeros((L, B, 2048), dtype=self.torch.float32, device=self.dev)
         ws_bytes = pkv.paged_decode_attn_workspace_size(B, 2048)
-        ws = self.torch.empty(max(ws_bytes, 16), dtype=self.torch.uint8, device=self.dev)
+        ws = self.torch.zeros(max(ws_bytes, 16), dtype=self.torch.uint8, device=self.dev)
         ctx_d = self.t(np.asarray(ctx, np.int32))
         for layer in range(L):
             bt = self.t(np.stack([tb[layer] for tb in tables]))
