@@ -108,6 +108,14 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m paged_kv_cache_172_amd.build` (needs hipcc)")
+    # torch ships its own HIP runtime under the same soname as the system's
+    # (libamdhip64.so.7).  Whichever is loaded first serves the whole process,
+    # and torch's bundled HSA runtime works only with its own, so torch (the
+    # caller's device memory and streams) is loaded before this library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, i32, i64, f32, f64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                              ctypes.c_double)
