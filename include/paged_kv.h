@@ -35,7 +35,8 @@
  *   - Pointers marked (device) are device memory of the current HIP device;
  *     (host) pointers are host memory.  All buffers belong to the caller;
  *     no call allocates or frees memory, and the library keeps no state
- *     besides a per-thread copy of the last HIP error text.
+ *     besides a per-thread copy of the last HIP error text and the fixed
+ *     scratch array of paged_kv_append_decode_attn_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued asynchronously on it; calls that share
  *     buffers must be ordered by the caller (same stream, or events).
@@ -308,6 +309,33 @@ int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_
                                 int64_t v_stride, const float* rope_cos, const float* rope_sin,
                                 int32_t max_pos, float scale, float* out, int64_t out_stride,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_kv_append_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It allocates nothing: when the
+ * plan needs partials (S > 1, which the plan only asks for below 64
+ * sequences), they and the merge counters live in a fixed device array of
+ * the library, 2,048 + 8 * 63 * 32 * 66 * 4 = 4,259,840 bytes, which holds
+ * the largest such plan.  Each GPU the library runs on holds its own copy
+ * until the process ends.  The first call on a device looks the array's
+ * address up and clears its counters with a small kernel on `stream`; every
+ * call leaves the counters zero again.  All calls on one GPU share that
+ * array: calls that overlap in time on one GPU (different streams, or
+ * threads) race and give wrong output rows; order them.  Arguments, results
+ * (bit for bit), preconditions and errors are those of
+ * paged_kv_append_decode_attn; WORKSPACE is returned only for a plan larger
+ * than the array, which valid arguments never produce.
+ */
+int paged_kv_append_decode_attn_noalloc(const paged_kv_pool* pool, const int32_t* block_table,
+                                        int64_t bt_stride, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t max_context_len,
+                                        const uint16_t* q, int64_t q_stride,
+                                        const uint16_t* k_new, int64_t k_stride,
+                                        const uint16_t* v_new, int64_t v_stride,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int32_t max_pos, float scale, float* out,
+                                        int64_t out_stride, void* stream);
 
 /* Text for a status code; for PKV_ERR_HIP it includes the last HIP error
  * text seen by this thread.  The pointer stays valid until the next call

@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     paged_decode_attn_workspace_size,
     paged_kv_append,
     paged_kv_append_decode_attn,
+    paged_kv_append_decode_attn_noalloc,
     paged_kv_prefill,
     paged_kv_copy_pages,
     paged_kv_rope_table,

@@ -34,6 +34,7 @@ EXPORTED = (
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
     "paged_kv_append_decode_attn",
+    "paged_kv_append_decode_attn_noalloc",
     "paged_kv_prefill",
     "paged_kv_copy_pages",
     "paged_kv_status_string",
@@ -134,6 +135,8 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_combine": ([P, i32, i32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_kv_append_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64, P, P,
                                          i32, f32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
+        "paged_kv_append_decode_attn_noalloc": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64,
+                                                 P, P, i32, f32, P, i64, P], ctypes.c_int),
         "paged_kv_prefill": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P, P, i32, P],
                              ctypes.c_int),
         "paged_kv_copy_pages": ([PP, P, P, i32, P], ctypes.c_int),
@@ -275,6 +278,17 @@ def paged_kv_append_decode_attn(pool: Pool, block_table, bt_stride, context_lens
         int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
         int(out_stride), _p(workspace), int(workspace_bytes), _stream(stream)),
         "paged_kv_append_decode_attn")
+
+
+def paged_kv_append_decode_attn_noalloc(pool: Pool, block_table, bt_stride, context_lens,
+                                        num_seqs, max_context_len, q, q_stride, k_new, k_stride,
+                                        v_new, v_stride, rope_cos, rope_sin, max_pos, scale, out,
+                                        out_stride, stream=None) -> None:
+    _check(load().paged_kv_append_decode_attn_noalloc(
+        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), int(num_seqs),
+        int(max_context_len), _p(q), int(q_stride), _p(k_new), int(k_stride), _p(v_new),
+        int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
+        int(out_stride), _stream(stream)), "paged_kv_append_decode_attn_noalloc")
 
 
 def paged_kv_prefill(pool: Pool, block_table, bt_stride, start_pos, cu_tokens, num_seqs,

@@ -384,6 +384,50 @@ int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_
     return hip_status(pkv::launch_append_attn_split(p, static_cast<hipStream_t>(stream)));
 }
 
+int paged_kv_append_decode_attn_noalloc(const paged_kv_pool* pool, const int32_t* block_table,
+                                        int64_t bt_stride, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t max_context_len,
+                                        const uint16_t* q, int64_t q_stride,
+                                        const uint16_t* k_new, int64_t k_stride,
+                                        const uint16_t* v_new, int64_t v_stride,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int32_t max_pos, float scale, float* out,
+                                        int64_t out_stride, void* stream) {
+    // Every argument is checked before any HIP call; the workspace check is
+    // against the fixed scratch (a stand-in pointer: only its size and
+    // alignment are looked at here).
+    const size_t need = num_seqs > 0 && pkv::plan_args_ok(num_seqs, max_context_len)
+                            ? pkv::workspace_bytes(num_seqs, max_context_len)
+                            : 0;
+    if (need > pkv::scratch_bytes()) return PKV_ERR_WORKSPACE;
+    static char stand_in alignas(16);
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+                             max_context_len, q, q_stride, scale, out, out_stride,
+                             need ? &stand_in : nullptr, need);
+    if (c.status != PKV_OK || num_seqs == 0) return c.status;
+    const int st = check_append(pool, block_table, bt_stride, context_lens, q, q_stride, k_new,
+                                k_stride, v_new, v_stride, rope_cos, rope_sin, max_pos);
+    if (st != PKV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    pkv::AttnParams& p = c.params;
+    if (need > 0) {
+        void* ws = nullptr;
+        const int hs = hip_status(pkv::scratch_buffer(&ws, s));
+        if (hs != PKV_OK) return hs;
+        set_workspace(p, ws);
+    }
+    p.k_pool_w = pool->k_pool;
+    p.v_pool_w = pool->v_pool;
+    p.k_new = k_new;
+    p.k_stride = k_stride;
+    p.v_new = v_new;
+    p.v_stride = v_stride;
+    p.rope_cos = rope_cos;
+    p.rope_sin = rope_sin;
+    p.max_pos = max_pos;
+    return hip_status(pkv::launch_append_attn_split(p, s));
+}
+
 const char* paged_kv_status_string(int status) {
     switch (status) {
         case PKV_OK: return "ok";

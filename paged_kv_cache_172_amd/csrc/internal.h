@@ -133,4 +133,10 @@ hipError_t launch_attn_split(const AttnParams& p, bool merge, hipStream_t stream
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);
 
+// The library's fixed device scratch (for callers that cannot allocate):
+// its size, and its address on the current device (looked up, and its
+// counters cleared on `stream`, on the first call per device).
+size_t scratch_bytes();
+hipError_t scratch_buffer(void** out, hipStream_t stream);
+
 }  // namespace pkv

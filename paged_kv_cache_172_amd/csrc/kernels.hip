@@ -21,6 +21,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace pkv {
@@ -993,7 +995,51 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
                     merge_dim(mw, xs[3], S));
 }
 
+// Zeroes n 32-bit words (the merge counters of the fixed scratch array).
+__global__ __launch_bounds__(256) void zero_words_kernel(int32_t* p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0;
+}
+
+// The fixed scratch of paged_kv_append_decode_attn_noalloc: the workspace of
+// the largest plan that uses one (S = kMaxSplits partials of kMergeSeqs - 1
+// sequences after the counter block), laid out as workspace_bytes()
+// describes.  Each device holds its own copy until the process ends.
+constexpr size_t kScratchBytes =
+    kCounterBytes + (size_t)kMaxSplits * (kMergeSeqs - 1) * kQHeads * kPartialFloats * sizeof(float);
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+size_t scratch_bytes() { return kScratchBytes; }
+
+// The device address of this device's scratch array.  In host code the
+// array's name is only a stand-in for it, so the address is looked up once
+// per device (with that device current) and kept; on that first call the
+// counter block is cleared by a fill kernel on the caller's stream.
+hipError_t scratch_buffer(void** out, hipStream_t stream) {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        const int words = (int)(kCounterBytes / sizeof(int32_t));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<int32_t*>(p), words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<1, AppendParams>),

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -259,6 +259,22 @@ def test_fused_rejects(lib, kw, want):
     a.update(kw)
     try:
         pkv.paged_kv_append_decode_attn(_pool(), **a)
+        got = pkv.PKV_OK
+    except pkv.PagedKVError as e:
+        got = e.status
+    assert got == want
+
+
+@pytest.mark.parametrize("kw,want", [c for c in FUSED_CASES if "workspace_bytes" not in c[0]])
+def test_fused_noalloc_rejects(lib, kw, want):
+    """The allocation-free fused call checks the same arguments, before any
+    HIP call (no scratch lookup for a rejected call)."""
+    a = dict(block_table=FAKE, bt_stride=128, context_lens=FAKE, num_seqs=4, max_context_len=2048,
+             q=FAKE, q_stride=Q_ROW, k_new=FAKE, k_stride=KV_ROW, v_new=FAKE, v_stride=KV_ROW,
+             rope_cos=FAKE, rope_sin=FAKE, max_pos=2048, scale=0.125, out=FAKE, out_stride=Q_ROW)
+    a.update(kw)
+    try:
+        pkv.paged_kv_append_decode_attn_noalloc(_pool(), **a)
         got = pkv.PKV_OK
     except pkv.PagedKVError as e:
         got = e.status
