@@ -129,10 +129,14 @@ def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
 def time_continuous_batching(torch, stream, rope, reps: int):
     """The continuous-batching mix: 256 sequences x 16 layers, context lengths
     log-uniform in 16..2,048, 16 of them opening a page this step (lazy page
-    step first).  The fused step per layer, with the batch in its given order
-    and ordered longest-first by the caller (the kernels' results do not
-    depend on the order; with 2,048 (sequence, KV head) workgroups, twice what
-    the GPU holds at once, the order sets the tail)."""
+    step first).  The fused step, timed per layer, in three ways: the batch as
+    given, ranked once per step by the library (paged_decode_attn_order, its
+    launch inside the timed step) and followed by every layer's call
+    (``given_order``); the batch as given with no order
+    (``given_order_unranked``); and sorted longest-first by the caller
+    (``longest_first``).  The kernels' results do not depend on the order;
+    with 2,048 (sequence, KV head) workgroups, twice what the GPU holds at
+    once, the order sets the tail."""
     from paged_kv_cache_172_amd import pages as pg, workload as wl
     from paged_kv_cache_172_amd.runner import DecodeBatch
     spec = wl.config_spec(4)
@@ -147,7 +151,8 @@ def time_continuous_batching(torch, stream, rope, reps: int):
                        f"(sum {int(spec.ctx.sum())} tokens per layer)",
            "kv_bytes_per_layer": int(kv_layer)}
     longest = np.argsort(-spec.ctx, kind="stable")
-    for name, perm in (("given_order", None), ("longest_first", longest)):
+    for name, perm, ranked in (("given_order", None, True), ("given_order_unranked", None, False),
+                               ("longest_first", longest, False)):
         if perm is None:
             args = (bt, spec.ctx, q0, k0, v0)
         else:
@@ -155,20 +160,19 @@ def time_continuous_batching(torch, stream, rope, reps: int):
                     *(np.ascontiguousarray(x[:, perm]) for x in (q0, k0, v0)))
         b = DecodeBatch(pool, *args, rope=rope, max_context_len=wl.MAX_CONTEXT)
         for _ in range(PREWARM_STEPS // 4):
-            for layer in range(L):
-                b.append_attn(layer, stream)
+            b.step_fused(stream, order=ranked)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(reps):
-            for layer in range(L):
-                b.append_attn(layer, stream)
+            b.step_fused(stream, order=ranked)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / (reps * L) * 1e3
         res[name] = {"us_per_layer": round(us, 2), "kv_gbps": round(kv_layer / (us * 1e-6) / 1e9, 1),
-                     "frac_of_peak": round(kv_layer / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+                     "frac_of_peak": round(kv_layer / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "library_order": ranked}
         del b
     del pool
     torch.cuda.empty_cache()

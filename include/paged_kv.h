@@ -199,6 +199,27 @@ int paged_kv_copy_pages(const paged_kv_pool* pool, const int32_t* src, const int
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
 
 /*
+ * Start order of a decode batch whose lengths differ ([HN-batch]: each
+ * sequence has its own attention length).  When a launch has more
+ * workgroups than the GPU holds at once, they start in rank order, and a
+ * long sequence that starts late sets the end of the launch; started
+ * longest first, the long ones overlap the short ones.  Writes
+ * seq_order[r] = the sequence of rank r, by descending page count
+ * ceil(min(context_lens[s], max_context_len) / 16), ties in batch order --
+ * a permutation of [0, num_seqs), computed on the device by one small
+ * launch.  Lengths are the same for every layer of a decode step, so one
+ * call per step serves all its layers' attention calls (pass seq_order to
+ * them).  The attention follows the order only when its workgroups exceed
+ * what the GPU holds at once; the order never changes a result bit.
+ *   context_lens  (device) int32 [num_seqs]
+ *   seq_order     (device) int32 [num_seqs], written
+ * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
+ * [1, 2048]), HIP.  num_seqs == 0: no-op.
+ */
+int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t* seq_order, void* stream);
+
+/*
  * Bytes of device workspace paged_decode_attn needs for this plan: 0 when
  * S == 1, else 2048 + S * num_seqs * 32 * 66 * 4.  The first 2048 bytes are
  * 512 int32 counters, one per (sequence, KV head) for up to 64 sequences
@@ -244,6 +265,10 @@ int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, vo
  * past ceil(n/16) may hold any value, which is never used.  A table entry
  * below ceil(n/16) that is not a page in [0, num_pages) is not dereferenced;
  * that sequence's rows come out NaN.
+ *   seq_order        (device) int32 [num_seqs] from paged_decode_attn_order, or
+ *                    NULL: the order in which sequences are started (see there).
+ *                    It changes no result bit; an entry outside [0, num_seqs)
+ *                    counts as its own rank.
  *   max_context_len  host-known upper bound of every context_lens[s] (drives the plan)
  *   q                (device) BF16 [num_seqs][q_stride], already rotated
  *   out              (device) FP32 [num_seqs][out_stride], >= 2048 per row
@@ -258,7 +283,8 @@ int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, vo
  * num_seqs == 0: no-op.
  */
 int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
-                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                      int32_t max_context_len,
                       const uint16_t* q, int64_t q_stride, float scale, float* out,
                       int64_t out_stride, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -276,7 +302,8 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
  * WORKSPACE).
  */
 int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
-                            int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int64_t bt_stride, const int32_t* context_lens,
+                            const int32_t* seq_order, int32_t num_seqs,
                             int32_t max_context_len, const uint16_t* q, int64_t q_stride,
                             float scale, float* out, int64_t out_stride, void* workspace,
                             size_t workspace_bytes, void* stream);
@@ -293,9 +320,9 @@ int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
  *     paged_kv_append(pool, block_table, bt_stride, context_lens, num_seqs,
  *                     q, q_stride, k_new, k_stride, v_new, v_stride,
  *                     rope_cos, rope_sin, max_pos, stream);
- *     paged_decode_attn(pool, block_table, bt_stride, context_lens, num_seqs,
- *                       max_context_len, q, q_stride, scale, out, out_stride,
- *                       workspace, workspace_bytes, stream);
+ *     paged_decode_attn(pool, block_table, bt_stride, context_lens, seq_order,
+ *                       num_seqs, max_context_len, q, q_stride, scale, out,
+ *                       out_stride, workspace, workspace_bytes, stream);
  * except that q is only read: the rotated q is used but not written back.
  * A new token past max_context_len is still written to its page and, as in
  * the two calls, not attended.  Arguments, preconditions and errors are
@@ -303,7 +330,8 @@ int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
  * num_seqs == 0: no-op.
  */
 int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_table,
-                                int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                                int64_t bt_stride, const int32_t* context_lens,
+                                const int32_t* seq_order, int32_t num_seqs,
                                 int32_t max_context_len, const uint16_t* q, int64_t q_stride,
                                 const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
                                 int64_t v_stride, const float* rope_cos, const float* rope_sin,
@@ -329,7 +357,8 @@ int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_
  */
 int paged_kv_append_decode_attn_noalloc(const paged_kv_pool* pool, const int32_t* block_table,
                                         int64_t bt_stride, const int32_t* context_lens,
-                                        int32_t num_seqs, int32_t max_context_len,
+                                        const int32_t* seq_order, int32_t num_seqs,
+                                        int32_t max_context_len,
                                         const uint16_t* q, int64_t q_stride,
                                         const uint16_t* k_new, int64_t k_stride,
                                         const uint16_t* v_new, int64_t v_stride,

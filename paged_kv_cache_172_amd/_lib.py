@@ -30,6 +30,7 @@ EXPORTED = (
     "paged_decode_attn_num_splits",
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace_init",
+    "paged_decode_attn_order",
     "paged_decode_attn",
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
@@ -128,15 +129,17 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_num_splits": ([i32, i32], i32),
         "paged_decode_attn_workspace_size": ([i32, i32], ctypes.c_size_t),
         "paged_decode_attn_workspace_init": ([P, ctypes.c_size_t, P], ctypes.c_int),
-        "paged_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, f32, P, i64, P, ctypes.c_size_t,
-                               P], ctypes.c_int),
-        "paged_decode_attn_split": ([PP, P, i64, P, i32, i32, P, i64, f32, P, i64, P,
+        "paged_decode_attn_order": ([P, i32, i32, P, P], ctypes.c_int),
+        "paged_decode_attn": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
+                               ctypes.c_size_t, P], ctypes.c_int),
+        "paged_decode_attn_split": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
                                      ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_combine": ([P, i32, i32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
-        "paged_kv_append_decode_attn": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64, P, P,
-                                         i32, f32, P, i64, P, ctypes.c_size_t, P], ctypes.c_int),
-        "paged_kv_append_decode_attn_noalloc": ([PP, P, i64, P, i32, i32, P, i64, P, i64, P, i64,
-                                                 P, P, i32, f32, P, i64, P], ctypes.c_int),
+        "paged_kv_append_decode_attn": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P,
+                                         P, i32, f32, P, i64, P, ctypes.c_size_t, P],
+                                        ctypes.c_int),
+        "paged_kv_append_decode_attn_noalloc": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P,
+                                                 i64, P, P, i32, f32, P, i64, P], ctypes.c_int),
         "paged_kv_prefill": ([PP, P, i64, P, P, i32, i32, P, i64, P, i64, P, i64, P, P, i32, P],
                              ctypes.c_int),
         "paged_kv_copy_pages": ([PP, P, P, i32, P], ctypes.c_int),
@@ -238,27 +241,37 @@ def paged_decode_attn_workspace_init(workspace, workspace_bytes, stream=None) ->
            "paged_decode_attn_workspace_init")
 
 
-def _attn_args(pool, block_table, bt_stride, context_lens, num_seqs, max_context_len, q,
-               q_stride, scale, out, out_stride, workspace, workspace_bytes, stream):
-    return (ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens),
+def paged_decode_attn_order(context_lens, num_seqs, max_context_len, seq_order,
+                            stream=None) -> None:
+    _check(load().paged_decode_attn_order(_p(context_lens), int(num_seqs), int(max_context_len),
+                                          _p(seq_order), _stream(stream)),
+           "paged_decode_attn_order")
+
+
+def _attn_args(pool, block_table, bt_stride, context_lens, seq_order, num_seqs, max_context_len,
+               q, q_stride, scale, out, out_stride, workspace, workspace_bytes, stream):
+    return (ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), _p(seq_order),
             int(num_seqs), int(max_context_len), _p(q), int(q_stride), float(scale), _p(out),
             int(out_stride), _p(workspace), int(workspace_bytes), _stream(stream))
 
 
 def paged_decode_attn(pool: Pool, block_table, bt_stride, context_lens, num_seqs,
                       max_context_len, q, q_stride, scale, out, out_stride, workspace=None,
-                      workspace_bytes=0, stream=None) -> None:
+                      workspace_bytes=0, stream=None, seq_order=None) -> None:
+    """seq_order (the C argument after context_lens) is a keyword here."""
     _check(load().paged_decode_attn(*_attn_args(
-        pool, block_table, bt_stride, context_lens, num_seqs, max_context_len, q, q_stride,
-        scale, out, out_stride, workspace, workspace_bytes, stream)), "paged_decode_attn")
+        pool, block_table, bt_stride, context_lens, seq_order, num_seqs, max_context_len, q,
+        q_stride, scale, out, out_stride, workspace, workspace_bytes, stream)),
+        "paged_decode_attn")
 
 
 def paged_decode_attn_split(pool: Pool, block_table, bt_stride, context_lens, num_seqs,
                             max_context_len, q, q_stride, scale, out, out_stride, workspace=None,
-                            workspace_bytes=0, stream=None) -> None:
+                            workspace_bytes=0, stream=None, seq_order=None) -> None:
     _check(load().paged_decode_attn_split(*_attn_args(
-        pool, block_table, bt_stride, context_lens, num_seqs, max_context_len, q, q_stride,
-        scale, out, out_stride, workspace, workspace_bytes, stream)), "paged_decode_attn_split")
+        pool, block_table, bt_stride, context_lens, seq_order, num_seqs, max_context_len, q,
+        q_stride, scale, out, out_stride, workspace, workspace_bytes, stream)),
+        "paged_decode_attn_split")
 
 
 def paged_decode_attn_combine(context_lens, num_seqs, max_context_len, out, out_stride,
@@ -271,9 +284,11 @@ def paged_decode_attn_combine(context_lens, num_seqs, max_context_len, out, out_
 def paged_kv_append_decode_attn(pool: Pool, block_table, bt_stride, context_lens, num_seqs,
                                 max_context_len, q, q_stride, k_new, k_stride, v_new, v_stride,
                                 rope_cos, rope_sin, max_pos, scale, out, out_stride,
-                                workspace=None, workspace_bytes=0, stream=None) -> None:
+                                workspace=None, workspace_bytes=0, stream=None,
+                                seq_order=None) -> None:
     _check(load().paged_kv_append_decode_attn(
-        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), int(num_seqs),
+        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), _p(seq_order),
+        int(num_seqs),
         int(max_context_len), _p(q), int(q_stride), _p(k_new), int(k_stride), _p(v_new),
         int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
         int(out_stride), _p(workspace), int(workspace_bytes), _stream(stream)),
@@ -283,9 +298,10 @@ def paged_kv_append_decode_attn(pool: Pool, block_table, bt_stride, context_lens
 def paged_kv_append_decode_attn_noalloc(pool: Pool, block_table, bt_stride, context_lens,
                                         num_seqs, max_context_len, q, q_stride, k_new, k_stride,
                                         v_new, v_stride, rope_cos, rope_sin, max_pos, scale, out,
-                                        out_stride, stream=None) -> None:
+                                        out_stride, stream=None, seq_order=None) -> None:
     _check(load().paged_kv_append_decode_attn_noalloc(
-        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), int(num_seqs),
+        ctypes.byref(pool), _p(block_table), int(bt_stride), _p(context_lens), _p(seq_order),
+        int(num_seqs),
         int(max_context_len), _p(q), int(q_stride), _p(k_new), int(k_stride), _p(v_new),
         int(v_stride), _p(rope_cos), _p(rope_sin), int(max_pos), float(scale), _p(out),
         int(out_stride), _stream(stream)), "paged_kv_append_decode_attn_noalloc")

@@ -113,13 +113,26 @@ void set_workspace(pkv::AttnParams& p, void* workspace) {
     p.ws_ml = reinterpret_cast<float2*>(base + pkv::kCounterBytes + acc_bytes);
 }
 
+// Whether an attention launch follows the caller's sequence order: only
+// when its workgroups do not all fit on the device at once (the order then
+// decides which ones start first; otherwise every workgroup starts at once
+// and reading the order would only delay each start).  The resident count
+// is the occupancy of the attention kernel times the compute units, looked
+// up once per device.
+bool use_order(const int32_t* seq_order, int32_t num_seqs, const pkv::Plan& plan) {
+    if (!seq_order) return false;
+    const int64_t grid = (int64_t)num_seqs * pkv::kKVHeads * plan.splits;
+    return grid > pkv::resident_workgroups();
+}
+
 struct AttnCheck {
     int status;
     pkv::AttnParams params;
 };
 
 AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                     const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                     int32_t max_context_len,
                      const uint16_t* q, int64_t q_stride, float scale, float* out,
                      int64_t out_stride, void* workspace, size_t workspace_bytes) {
     AttnCheck r{};
@@ -156,6 +169,7 @@ AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int6
         }
     }
     pkv::AttnParams& p = r.params;
+    p.plan = pkv::make_plan(num_seqs, max_context_len);
     p.k_pool = pool->k_pool;
     p.v_pool = pool->v_pool;
     p.num_pages = pool->num_pages;
@@ -167,10 +181,10 @@ AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int6
     p.context_lens = context_lens;
     p.num_seqs = num_seqs;
     p.max_context_len = max_context_len;
+    p.seq_order = use_order(seq_order, num_seqs, p.plan) ? seq_order : nullptr;
     p.q = q;
     p.q_stride = q_stride;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale / ln 2
-    p.plan = pkv::make_plan(num_seqs, max_context_len);
     p.out = out;
     p.out_stride = out_stride;
     if (need > 0) set_workspace(p, workspace);
@@ -301,6 +315,16 @@ size_t paged_decode_attn_workspace_size(int32_t num_seqs, int32_t max_context_le
     return pkv::workspace_bytes(num_seqs, max_context_len);
 }
 
+int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t* seq_order, void* stream) {
+    if (num_seqs < 0) return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PKV_OK;
+    if (!context_lens || !seq_order || max_context_len < 1 || max_context_len > pkv::kMaxContext)
+        return PKV_ERR_INVALID_ARG;
+    return hip_status(pkv::launch_order(context_lens, num_seqs, max_context_len, seq_order,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
     if (workspace_bytes == 0) return PKV_OK;
     if (!workspace) return PKV_ERR_INVALID_ARG;
@@ -310,11 +334,12 @@ int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, vo
 }
 
 int paged_decode_attn_split(const paged_kv_pool* pool, const int32_t* block_table,
-                            int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                            int64_t bt_stride, const int32_t* context_lens,
+                            const int32_t* seq_order, int32_t num_seqs,
                             int32_t max_context_len, const uint16_t* q, int64_t q_stride,
                             float scale, float* out, int64_t out_stride, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, seq_order, num_seqs,
                              max_context_len, q, q_stride, scale, out, out_stride, workspace,
                              workspace_bytes);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;
@@ -347,10 +372,11 @@ int paged_decode_attn_combine(const int32_t* context_lens, int32_t num_seqs,
 }
 
 int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int64_t bt_stride,
-                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      const int32_t* context_lens, const int32_t* seq_order, int32_t num_seqs,
+                      int32_t max_context_len,
                       const uint16_t* q, int64_t q_stride, float scale, float* out,
                       int64_t out_stride, void* workspace, size_t workspace_bytes, void* stream) {
-    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, seq_order, num_seqs,
                              max_context_len, q, q_stride, scale, out, out_stride, workspace,
                              workspace_bytes);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;
@@ -358,13 +384,14 @@ int paged_decode_attn(const paged_kv_pool* pool, const int32_t* block_table, int
 }
 
 int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_table,
-                                int64_t bt_stride, const int32_t* context_lens, int32_t num_seqs,
+                                int64_t bt_stride, const int32_t* context_lens,
+                                const int32_t* seq_order, int32_t num_seqs,
                                 int32_t max_context_len, const uint16_t* q, int64_t q_stride,
                                 const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
                                 int64_t v_stride, const float* rope_cos, const float* rope_sin,
                                 int32_t max_pos, float scale, float* out, int64_t out_stride,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, seq_order, num_seqs,
                              max_context_len, q, q_stride, scale, out, out_stride, workspace,
                              workspace_bytes);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;
@@ -386,7 +413,8 @@ int paged_kv_append_decode_attn(const paged_kv_pool* pool, const int32_t* block_
 
 int paged_kv_append_decode_attn_noalloc(const paged_kv_pool* pool, const int32_t* block_table,
                                         int64_t bt_stride, const int32_t* context_lens,
-                                        int32_t num_seqs, int32_t max_context_len,
+                                        const int32_t* seq_order, int32_t num_seqs,
+                                        int32_t max_context_len,
                                         const uint16_t* q, int64_t q_stride,
                                         const uint16_t* k_new, int64_t k_stride,
                                         const uint16_t* v_new, int64_t v_stride,
@@ -401,7 +429,7 @@ int paged_kv_append_decode_attn_noalloc(const paged_kv_pool* pool, const int32_t
                             : 0;
     if (need > pkv::scratch_bytes()) return PKV_ERR_WORKSPACE;
     static char stand_in alignas(16);
-    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, num_seqs,
+    AttnCheck c = check_attn(pool, block_table, bt_stride, context_lens, seq_order, num_seqs,
                              max_context_len, q, q_stride, scale, out, out_stride,
                              need ? &stand_in : nullptr, need);
     if (c.status != PKV_OK || num_seqs == 0) return c.status;

@@ -85,7 +85,10 @@ struct Plan {
 // finished workgroups of each (sequence, KV head) in a fixed block of
 // kMergeSeqs * 8 int32 counters at the start of the workspace, whatever
 // num_seqs is, so that every call finds its counters at the same place.
-constexpr int64_t kPlanTargetWaves = 2048;
+#ifndef PKV_TARGET_WAVES
+#define PKV_TARGET_WAVES 2048
+#endif
+constexpr int64_t kPlanTargetWaves = PKV_TARGET_WAVES;
 constexpr int kMergeSeqs = (int)(kPlanTargetWaves / (kKVHeads * kChunkWaves));
 constexpr size_t kCounterBytes = (size_t)kMergeSeqs * kKVHeads * sizeof(int32_t);
 static_assert(kCounterBytes % 256 == 0, "partials start 256-byte aligned");
@@ -97,6 +100,7 @@ struct AttnParams {
     const int32_t* block_table;
     int64_t bt_stride;
     const int32_t* context_lens;
+    const int32_t* seq_order;   // rank -> sequence, or null (batch order)
     int32_t num_seqs;
     int32_t max_context_len;
     const uint16_t* q;
@@ -132,6 +136,15 @@ hipError_t launch_copy_pages(const CopyParams& p, hipStream_t stream);
 hipError_t launch_attn_split(const AttnParams& p, bool merge, hipStream_t stream);
 hipError_t launch_append_attn_split(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(const AttnParams& p, hipStream_t stream);
+
+// Ranks the sequences of a batch for the attention launches: seq_order[r]
+// is the sequence of rank r, by descending page count (of the length clamped
+// to max_context_len), ties by index.  One workgroup.
+hipError_t launch_order(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                        int32_t* seq_order, hipStream_t stream);
+// Attention workgroups the current device holds at once (looked up once per
+// device); INT64_MAX when the query fails.
+int64_t resident_workgroups();
 
 // The library's fixed device scratch (for callers that cannot allocate):
 // its size, and its address on the current device (looked up, and its

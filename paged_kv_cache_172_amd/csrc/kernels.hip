@@ -730,11 +730,19 @@ void attn_split_kernel(AttnParams p) {
 
     const int lane = threadIdx.x & 63;
     const int w = uniform((int)(threadIdx.x >> 6));
-    const uint32_t wg = blockIdx.x;                    // g fastest, then s, then outer chunk
+    const uint32_t wg = blockIdx.x;                    // g fastest, then rank, then outer chunk
     const int g = (int)(wg % kKVHeads);
     const uint32_t rest = wg / kKVHeads;
-    const int s = (int)(rest % (uint32_t)p.num_seqs);
+    const int rank = (int)(rest % (uint32_t)p.num_seqs);
     const int ci = (int)(rest / (uint32_t)p.num_seqs);
+    // The sequence of this rank: the caller's order when given (started in
+    // that order, so the longest sequences do not start last), else batch
+    // order.  An entry outside [0, num_seqs) falls back to the rank itself.
+    int s = rank;
+    if (p.seq_order) {
+        const int o = uniform(p.seq_order[rank]);
+        s = o >= 0 && o < p.num_seqs ? o : rank;
+    }
     const int t = lane & 15;   // token slot of this lane (the MFMA column)
     const int c4 = lane >> 4;  // dims 8*c4..8*c4+7 and 32+8*c4..32+8*c4+7 (the MFMA k slice)
 
@@ -995,6 +1003,80 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
                     merge_dim(mw, xs[3], S));
 }
 
+// ----------------------------------------------------------- ordering --
+//
+// One workgroup ranks the num_seqs sequences by descending page count
+// (stable: ties keep batch order), a counting sort over the 129 possible
+// counts.  Rounds of 1,024 sequences, one per thread: a thread's place is
+// the start of its count's range, plus its count's members in earlier
+// rounds, in earlier waves of this round, and in lower lanes of its own wave
+// (lanes with the same count found with one ballot per bit of the count).
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderBins = kMaxContext / kPageTokens + 1;   // page counts 0..128
+static_assert(kOrderBins <= 255, "counts fit 8 bits; 255 marks no sequence");
+
+__device__ __forceinline__ int page_bin(const int32_t* ctx, int s, int max_context_len) {
+    const int c = ctx[s];
+    const int n = c < max_context_len ? c : max_context_len;
+    return n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx, int num_seqs, int max_context_len,
+                                                              int32_t* order) {
+    __shared__ int start[kOrderBins];                 // first rank of each count, this round
+    __shared__ int wave_count[kOrderWaves][kOrderBins];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    for (int b = tid; b < kOrderBins; b += kOrderThreads) start[b] = 0;
+    for (int i = tid; i < kOrderWaves * kOrderBins; i += kOrderThreads) (&wave_count[0][0])[i] = 0;
+    __syncthreads();
+    // histogram (start[] doubles as the count of each bin)
+    for (int s = tid; s < num_seqs; s += kOrderThreads) atomicAdd(&start[page_bin(ctx, s, max_context_len)], 1);
+    __syncthreads();
+    if (tid == 0) {   // exclusive prefix, longest first
+        int run = 0;
+        for (int b = kOrderBins - 1; b >= 0; --b) {
+            const int c = start[b];
+            start[b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r0 = 0; r0 < num_seqs; r0 += kOrderThreads) {
+        const int s = r0 + tid;
+        const bool valid = s < num_seqs;
+        const int key = valid ? page_bin(ctx, s, max_context_len) : 255;
+        uint64_t same = ~0ull;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool bit = (key >> k) & 1;
+            const uint64_t b = __builtin_amdgcn_ballot_w64(bit);
+            same &= bit ? b : ~b;
+        }
+        const int lower = __builtin_popcountll(same & below);
+        if (valid && lower == 0) wave_count[wv][key] = __builtin_popcountll(same);
+        __syncthreads();
+        if (valid) {
+            int pre = 0;
+            for (int v = 0; v < wv; ++v) pre += wave_count[v][key];
+            order[start[key] + pre + lower] = s;
+        }
+        __syncthreads();
+        for (int b = tid; b < kOrderBins; b += kOrderThreads) {
+            int c = 0;
+            for (int v = 0; v < kOrderWaves; ++v) {
+                c += wave_count[v][b];
+                wave_count[v][b] = 0;
+            }
+            start[b] += c;
+        }
+        __syncthreads();
+    }
+}
+
 // Zeroes n 32-bit words (the merge counters of the fixed scratch array).
 __global__ __launch_bounds__(256) void zero_words_kernel(int32_t* p, int n) {
     const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
@@ -1013,6 +1095,32 @@ constexpr int kMaxDevices = 64;
 }  // namespace
 
 size_t scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_order(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                        int32_t* seq_order, hipStream_t stream) {
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, context_lens, num_seqs,
+                       max_context_len, seq_order);
+    return hipGetLastError();
+}
+
+int64_t resident_workgroups() {
+    static std::mutex mu;
+    static int64_t cached[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return INT64_MAX;
+    std::lock_guard<std::mutex> g(mu);
+    if (!cached[dev]) {
+        int per_cu = 0, cus = 0;
+        // the fused kernel holds the most resources of the attention variants
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<true, true>,
+                                                         kChunkWaves * 64, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            per_cu < 1 || cus < 1)
+            return INT64_MAX;
+        cached[dev] = (int64_t)per_cu * cus;
+    }
+    return cached[dev];
+}
 
 // The device address of this device's scratch array.  In host code the
 // array's name is only a stand-in for it, so the address is looked up once

@@ -69,6 +69,10 @@ class DecodeBatch:
                                               torch.cuda.current_stream(self.device))
         base = self.pool_pages.data_ptr()
         self.pool = _lib.make_pool(base, base + HALF_PAGE * 2, P, PAGE_ELEMS, 16 * 64, 64)
+        # start order of the sequences (paged_decode_attn_order), used by the
+        # attention calls once order() has run
+        self.seq_order = torch.empty(self.num_seqs, dtype=torch.int32, device=self.device)
+        self.ordered = False
 
     @property
     def splits(self) -> int:
@@ -89,6 +93,17 @@ class DecodeBatch:
         import torch
         return stream if stream is not None else torch.cuda.current_stream(self.device)
 
+    def order(self, stream=None) -> None:
+        """Rank the sequences once for this step's attention calls (longest
+        first); every later attention call of this batch starts them in that
+        order."""
+        _lib.paged_decode_attn_order(self.context_lens, self.num_seqs, self.max_context_len,
+                                     self.seq_order, self._stream(stream))
+        self.ordered = True
+
+    def _order(self):
+        return self.seq_order if self.ordered else None
+
     def append(self, layer: int, stream=None) -> None:
         _lib.paged_kv_append(
             self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
@@ -99,13 +114,15 @@ class DecodeBatch:
         _lib.paged_decode_attn(
             self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
             self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream))
+            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
+            seq_order=self._order())
 
     def attn_split(self, layer: int, stream=None) -> None:
         _lib.paged_decode_attn_split(
             self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
             self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream))
+            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
+            seq_order=self._order())
 
     def attn_combine(self, layer: int, stream=None) -> None:
         _lib.paged_decode_attn_combine(
@@ -118,7 +135,8 @@ class DecodeBatch:
             self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
             self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.k[layer], KV_ROW,
             self.v[layer], KV_ROW, self.rope_cos, self.rope_sin, self.max_pos, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream))
+            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
+            seq_order=self._order())
 
     def step(self, stream=None) -> None:
         """One decode step: for every layer, append then attention."""
@@ -126,7 +144,10 @@ class DecodeBatch:
             self.append(layer, stream)
             self.attn(layer, stream)
 
-    def step_fused(self, stream=None) -> None:
-        """One decode step with the fused call per layer."""
+    def step_fused(self, stream=None, order: bool = False) -> None:
+        """One decode step with the fused call per layer; with order, the
+        sequences are ranked once first (paged_decode_attn_order)."""
+        if order:
+            self.order(stream)
         for layer in range(self.num_layers):
             self.append_attn(layer, stream)

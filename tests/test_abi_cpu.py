@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -214,6 +214,23 @@ def test_combine_rejects(lib):
     # a single-chunk plan has nothing to merge: returns OK without launching
     assert pkv.paged_decode_attn_num_splits(4096, 64) == 1
     assert st(num_seqs=4096, max_context_len=64, workspace=None) == pkv.PKV_OK
+
+
+def test_order_rejects(lib):
+    def st(**kw):
+        a = dict(context_lens=FAKE, num_seqs=4, max_context_len=2048, seq_order=FAKE)
+        a.update(kw)
+        try:
+            pkv.paged_decode_attn_order(**a)
+        except pkv.PagedKVError as e:
+            return e.status
+        return pkv.PKV_OK
+    assert st(num_seqs=0) == pkv.PKV_OK
+    assert st(num_seqs=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert st(context_lens=None) == pkv.PKV_ERR_INVALID_ARG
+    assert st(seq_order=None) == pkv.PKV_ERR_INVALID_ARG
+    assert st(max_context_len=0) == pkv.PKV_ERR_INVALID_ARG
+    assert st(max_context_len=2049) == pkv.PKV_ERR_INVALID_ARG
 
 
 def test_workspace_init_rejects(lib):
