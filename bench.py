@@ -435,6 +435,10 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated measurement legs beside the headline step: prefill, "
+                         "prefix, mix (config 4), configs (1, 2, 5); 'all' (default) or 'none'. "
+                         "The headline step and its roofline are always timed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device copies of 256 MiB (reference for HBM byte counters)")
     a = ap.parse_args()
@@ -526,9 +530,12 @@ def main():
     split_avg = timed(lambda: [batch.attn_split(layer, stream) for layer in range(L)], a.steps) / L
     ms_unfused = timed(step_unfused, a.steps)
 
-    prefill = time_prefill(torch, pkv, stream, batch.rope_cos, batch.rope_sin, max(3, a.steps // 2))
-    prefix = time_prefix_sharing(torch, pkv, stream, max(3, a.steps))
-    mix = time_continuous_batching(torch, stream, rope, max(3, a.steps // 2))
+    legs = {"prefill", "prefix", "mix", "configs"} if a.legs == "all" else \
+        set() if a.legs == "none" else set(a.legs.split(","))
+    prefill = (time_prefill(torch, pkv, stream, batch.rope_cos, batch.rope_sin, max(3, a.steps // 2))
+               if "prefill" in legs else None)
+    prefix = time_prefix_sharing(torch, pkv, stream, max(3, a.steps)) if "prefix" in legs else None
+    mix = time_continuous_batching(torch, stream, rope, max(3, a.steps // 2)) if "mix" in legs else None
 
     kv_step = spec.kv_bytes_per_step()
     kv_layer = kv_step / L
@@ -575,7 +582,7 @@ def main():
             "alg_frac_of_peak": round(alg_split / (split_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "us_per_layer": round(split_avg * 1e3, 2),
             "seq_layers_per_s": round(spec.num_seqs / (split_avg * 1e-3), 1),
-            "combine_launched": splits > 1,
+            "in_kernel_merge": splits > 1,
         },
         "roofline": {
             "kernel": "attn_split_kernel<true, true> (fused append + attention)",
@@ -589,9 +596,10 @@ def main():
             "avg_launch_us": round(fused_avg * 1e3, 2),
         },
     }
-    result["prefill_fill"] = prefill
-    result["prefix_sharing"] = prefix
-    result["continuous_batching"] = mix
+    for key, leg in (("prefill_fill", prefill), ("prefix_sharing", prefix),
+                     ("continuous_batching", mix)):
+        if leg is not None:
+            result[key] = leg
     if free_stats:
         result["free_list"] = free_stats
     if not a.no_cpu_baseline:
@@ -600,14 +608,15 @@ def main():
     del batch, pool
     torch.cuda.empty_cache()
     others = {}
-    for k in (1, 2, 5):
+    for k in ((1, 2, 5) if "configs" in legs else ()):
         if k == a.config:
             continue
         log(f"[bench] config {k}")
         others[f"config{k}"] = time_small_or_stress_config(
             torch, k, stream, rope, reps=(200 if k < 5 else max(5, a.steps // 2)),
             cpu_budget_s=None if a.no_cpu_baseline else (3.0 if k < 5 else 6.0))
-    result["other_configs"] = others
+    if others:
+        result["other_configs"] = others
     print(json.dumps(result), flush=True)
 
 

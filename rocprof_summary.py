@@ -67,12 +67,12 @@ def trace_by_grid(db: str, kernel: str) -> str:
     per = defaultdict(list)
     for name, grid, dur in rows:
         if kernel in name:
-            per[int(grid)].append(dur / 1e3)
-    out = [f"| {kernel}: grid (work-items) | launches | median us | mean us | min us | max us |",
-           "|---|---|---|---|---|---|"]
-    for grid, d in sorted(per.items()):
-        out.append(f"| {grid} | {len(d)} | {statistics.median(d):.2f} | {sum(d) / len(d):.2f} | "
-                   f"{min(d):.2f} | {max(d):.2f} |")
+            per[(short(name), int(grid))].append(dur / 1e3)
+    out = ["| kernel | grid (work-items) | launches | median us | mean us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(per.items(), key=lambda kv: (kv[0][1], kv[0][0])):
+        out.append(f"| {name} | {grid} | {len(d)} | {statistics.median(d):.2f} | "
+                   f"{sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     return "\n".join(out)
 
 
