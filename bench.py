@@ -233,6 +233,32 @@ def time_prefix_sharing(torch, pkv, stream, reps: int):
     }
 
 
+def time_graph_step(torch, step, reps: int, layers: int):
+    """The same step captured once in a HIP graph and replayed: the graph
+    holds the step's launches and nothing else (no memory operations), and
+    replaying it submits them all at once.  `step(stream)` enqueues one step
+    on the stream it is given; capture and replay use a stream of their own
+    (capture cannot run on the default stream)."""
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        step(cap)
+    with torch.cuda.stream(cap):
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(cap)
+        for _ in range(reps):
+            g.replay()
+        e1.record(cap)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return {"ms_per_step": round(ms, 4), "us_per_layer": round(ms / layers * 1e3, 2)}
+
+
 def kernel_source_sha() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -377,9 +403,9 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * L) * 1e3      # us per layer
 
-    def fused():
+    def fused(s=stream):
         for layer in range(L):
-            b.append_attn(layer, stream)
+            b.append_attn(layer, s)
 
     def unfused():
         for layer in range(L):
@@ -399,6 +425,19 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
     us_u = timed(unfused)
     us_a = timed(attn)
     us_2 = timed(attn_two_phase)
+    gfused = time_graph_step(torch, fused, reps, L)["us_per_layer"]
+    tight = None
+    if k != 5 and int(spec.ctx.max()) < wl.MAX_CONTEXT:
+        # the plan drawn from the batch's own longest context, which a serving
+        # host knows: a 37-token sequence needs no split
+        bt_ = DecodeBatch(b.pool_pages, spec.block_tables, spec.ctx, q0, k0, v0, rope=rope,
+                          max_context_len=int(spec.ctx.max()))
+        b_save, b = b, bt_
+        tight = {"max_context_len": int(spec.ctx.max()), "splits": b.splits,
+                 "fused_us_per_layer": round(timed(fused), 2),
+                 "attn_us_per_layer": round(timed(attn), 2)}
+        b = b_save
+        del bt_
     kv_layer = spec.kv_bytes_per_step() / L
     res = {
         "workload": f"config {k}: {spec.name}",
@@ -409,9 +448,12 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         "unfused_us_per_layer": round(us_u, 2),
         "attn_us_per_layer": round(us_a, 2),
         "attn_split_then_combine_us_per_layer": round(us_2, 2),
+        "fused_graph_us_per_layer": gfused,
         "kv_gbps_fused": round(kv_layer / (us_f * 1e-6) / 1e9, 1),
         "kv_gbps_attn": round(kv_layer / (us_a * 1e-6) / 1e9, 1),
     }
+    if tight:
+        res["plan_from_batch_max"] = tight
     if k == 5:
         alg = split_bytes_per_launch(spec.ctx, b.splits) + append_bytes_per_launch(spec.num_seqs)
         res["frac_of_peak_fused"] = round(kv_layer / (us_f * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
@@ -481,9 +523,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    def step_fused():
+    def step_fused(s=stream):
         for layer in range(L):
-            batch.append_attn(layer, stream)
+            batch.append_attn(layer, s)
 
     def step_unfused():
         for layer in range(L):
@@ -522,11 +564,23 @@ def main():
     # does identical work whatever the order.
     ms_per_step = timed(step_fused, a.steps)
     assert torch.isfinite(batch.out).all(), "non-finite attention output"
+    # The distribution of steps, after the headline: an event recorded
+    # between consecutive steps on the stream (no synchronize in between),
+    # median and p10/p90 over the same number of steps.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(a.steps):
+        step_fused()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
     # The timed step is nothing but the dominant kernel, L launches back to
     # back on one stream between two HIP events, so its average launch
     # duration is the step time / L (it matches the profiler's kernel time).
     # The plain split kernel is timed the same way, on its own.
     fused_avg = ms_per_step / L
+    graph_leg = time_graph_step(torch, step_fused, a.steps, L)
     split_avg = timed(lambda: [batch.attn_split(layer, stream) for layer in range(L)], a.steps) / L
     ms_unfused = timed(step_unfused, a.steps)
 
@@ -555,6 +609,8 @@ def main():
         "warmup": a.warmup,
         "prewarm_steps": PREWARM_STEPS,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+        "graph_step": graph_leg,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

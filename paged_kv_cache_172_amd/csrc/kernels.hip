@@ -1034,14 +1034,23 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx
     __syncthreads();
     // histogram (start[] doubles as the count of each bin)
     for (int s = tid; s < num_seqs; s += kOrderThreads) atomicAdd(&start[page_bin(ctx, s, max_context_len)], 1);
+    // Exclusive prefix over the counts, longest first: an inclusive scan of
+    // the counts in descending-count order (position t holds count 128 - t),
+    // by doubling steps over 256 positions.
+    __shared__ int scan[256];
+    static_assert(kOrderBins <= 256, "one scan position per count");
+    __syncthreads();   // every count is in
+    if (tid < 256) scan[tid] = tid < kOrderBins ? start[kOrderBins - 1 - tid] : 0;
+    for (int off = 1; off < 256; off <<= 1) {
+        __syncthreads();
+        const int add = tid < 256 && tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        if (tid < 256) scan[tid] += add;
+    }
     __syncthreads();
-    if (tid == 0) {   // exclusive prefix, longest first
-        int run = 0;
-        for (int b = kOrderBins - 1; b >= 0; --b) {
-            const int c = start[b];
-            start[b] = run;
-            run += c;
-        }
+    if (tid < kOrderBins) {
+        const int b = kOrderBins - 1 - tid;
+        start[b] = scan[tid] - start[b];
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
