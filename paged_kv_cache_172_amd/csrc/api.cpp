@@ -125,6 +125,15 @@ bool use_order(const int32_t* seq_order, int32_t num_seqs, const pkv::Plan& plan
     return grid > pkv::resident_workgroups();
 }
 
+// Priority by pages left pays while the launch is at most two rounds of
+// resident workgroups: the critical path and the two workgroups that share a
+// CU then set its end.  Over many rounds of like workgroups the hardware's
+// oldest-first issue frees slots soonest, and it is left alone.
+bool priority_by_pages_left(int32_t num_seqs, const pkv::Plan& plan) {
+    const int64_t grid = (int64_t)num_seqs * pkv::kKVHeads * plan.splits;
+    return (grid + 1) / 2 <= pkv::resident_workgroups();
+}
+
 struct AttnCheck {
     int status;
     pkv::AttnParams params;
@@ -182,6 +191,7 @@ AttnCheck check_attn(const paged_kv_pool* pool, const int32_t* block_table, int6
     p.num_seqs = num_seqs;
     p.max_context_len = max_context_len;
     p.seq_order = use_order(seq_order, num_seqs, p.plan) ? seq_order : nullptr;
+    p.priority_by_pages_left = priority_by_pages_left(num_seqs, p.plan) ? 1 : 0;
     p.q = q;
     p.q_stride = q_stride;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale / ln 2

@@ -107,6 +107,10 @@ struct AttnParams {
     int64_t q_stride;
     float scale_log2;  // scale * log2(e): logits are kept in base-2 units
     Plan plan;
+    // Waves take their issue priority from the pages they have left (the
+    // most first); set when the grid is at most two rounds of what the GPU
+    // holds at once.
+    int32_t priority_by_pages_left;
     float* out;
     int64_t out_stride;
     float* ws_acc;     // [num_seqs][32][S][64]

@@ -715,6 +715,20 @@ static_assert(kRotTasks <= 64, "one task per lane");
 // S - 1 already counted merges the S partials into the output row (the
 // combine kernel's arithmetic, in the same order) and sets the counter back
 // to 0 for the next call.  No workgroup waits for another.
+// A wave's instruction-issue priority follows the pages it still has to
+// stream, the most first (set again before every ring round), in launches of
+// at most two rounds of resident workgroups.  Without it a CU's issue
+// arbitration favours the older of its workgroups at every tie: the older
+// finishes long before the younger, which then streams alone with half the
+// loads in flight, and short chunks compete with the long ones that set the
+// end of the launch.
+__device__ __forceinline__ void issue_priority(int pages_left) {
+    if (pages_left > 24) __builtin_amdgcn_s_setprio(3);
+    else if (pages_left > 16) __builtin_amdgcn_s_setprio(2);
+    else if (pages_left > 8) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 template <bool kFused, bool kMerge>
 __global__ __launch_bounds__(kChunkWaves * 64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
 void attn_split_kernel(AttnParams p) {
@@ -770,6 +784,7 @@ void attn_split_kernel(AttnParams p) {
     const int cs = (np + nchunks - 1) / nchunks;
     const int pb = (kChunkWaves * ci + w) * cs;
     const int pe = min(pb + cs, np);
+    if (p.priority_by_pages_left) issue_priority(pe - pb);
 
     // The fused append rotates only where append_kernel would (a token
     // position inside the RoPE table); otherwise q is used as given.
@@ -867,7 +882,11 @@ void attn_split_kernel(AttnParams p) {
         const float sl2 = p.scale_log2;
         int j = pb;
         const int rounds = (pe - 1 - pb) / kRing;   // whole rounds of unmasked pages
-        for (int r = 0; r < rounds; ++r) ring_round<kFused, 0>(ring, j, q, sl2, cx, st, issue);
+        for (int r = 0; r < rounds; ++r) {
+            if (p.priority_by_pages_left) issue_priority(pe - j);
+            ring_round<kFused, 0>(ring, j, q, sl2, cx, st, issue);
+        }
+        if (p.priority_by_pages_left) issue_priority(pe - j);
         ring.template at<kRing - 1>() = issue(j + kRing - 1);
         ring_tail<kFused, 0>(ring, j, pe - j, n, q, sl2, tok_page, cx, st);
         // The sum of head lane & 3 over the 4 lane rows (their tokens differ).
