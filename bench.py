@@ -392,15 +392,22 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
     L = spec.num_layers
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
+    host_us = {}
+
     def timed(fn):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
         e0.record(stream)
+        t0 = time.perf_counter()
         for _ in range(reps):
             fn()
+        t1 = time.perf_counter()
         e1.record(stream)
         torch.cuda.synchronize()
+        # the host's own time to enqueue the calls (Python, ctypes, the
+        # library's checks and the launch), per layer
+        host_us[fn.__name__] = round((t1 - t0) / (reps * L) * 1e6, 2)
         return e0.elapsed_time(e1) / (reps * L) * 1e3      # us per layer
 
     def fused(s=stream):
@@ -426,6 +433,7 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
     us_a = timed(attn)
     us_2 = timed(attn_two_phase)
     gfused = time_graph_step(torch, fused, reps, L)["us_per_layer"]
+    host_main = dict(host_us)
     tight = None
     if k != 5 and int(spec.ctx.max()) < wl.MAX_CONTEXT:
         # the plan drawn from the batch's own longest context, which a serving
@@ -436,6 +444,7 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         tight = {"max_context_len": int(spec.ctx.max()), "splits": b.splits,
                  "fused_us_per_layer": round(timed(fused), 2),
                  "attn_us_per_layer": round(timed(attn), 2)}
+        tight["host_enqueue_us_per_layer"] = {k: host_us[k] for k in ("fused", "attn")}
         b = b_save
         del bt_
     kv_layer = spec.kv_bytes_per_step() / L
@@ -449,6 +458,7 @@ def time_small_or_stress_config(torch, k: int, stream, rope, reps: int, cpu_budg
         "attn_us_per_layer": round(us_a, 2),
         "attn_split_then_combine_us_per_layer": round(us_2, 2),
         "fused_graph_us_per_layer": gfused,
+        "host_enqueue_us_per_layer": host_main,
         "kv_gbps_fused": round(kv_layer / (us_f * 1e-6) / 1e9, 1),
         "kv_gbps_attn": round(kv_layer / (us_a * 1e-6) / 1e9, 1),
     }

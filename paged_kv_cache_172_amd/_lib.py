@@ -174,20 +174,20 @@ def load(path: str = LIB_PATH):
 
 
 def _p(x):
-    """Device pointer of a tensor-like (data_ptr()) or a plain int; None -> NULL."""
-    if x is None:
-        return None
-    if hasattr(x, "data_ptr"):
-        return ctypes.c_void_p(x.data_ptr())
-    return ctypes.c_void_p(int(x))
+    """Device pointer of a tensor-like (data_ptr()) or a plain int, as an int
+    (the declared c_void_p arguments take ints); None -> NULL."""
+    if x is None or type(x) is int:
+        return x
+    dp = getattr(x, "data_ptr", None)
+    return dp() if dp is not None else int(x)
 
 
 def _stream(stream):
-    if stream is None:
-        return None
-    if hasattr(stream, "cuda_stream"):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+    """A stream object (cuda_stream), a raw handle (int) or None (NULL)."""
+    if stream is None or type(stream) is int:
+        return stream
+    cs = getattr(stream, "cuda_stream", None)
+    return cs if cs is not None else int(stream)
 
 
 def _check(status: int, where: str) -> int:
@@ -201,8 +201,7 @@ def status_string(status: int) -> str:
 
 
 def make_pool(k_pool, v_pool, num_pages, page_stride, head_stride, slot_stride) -> Pool:
-    kp, vp = _p(k_pool), _p(v_pool)
-    return Pool(kp.value if kp is not None else None, vp.value if vp is not None else None,
+    return Pool(_p(k_pool), _p(v_pool),
                 int(num_pages), int(page_stride), int(head_stride), int(slot_stride))
 
 

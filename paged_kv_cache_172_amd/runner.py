@@ -73,6 +73,18 @@ class DecodeBatch:
         # attention calls once order() has run
         self.seq_order = torch.empty(self.num_seqs, dtype=torch.int32, device=self.device)
         self.ordered = False
+        # Every device address a call passes, as a plain int, per layer where
+        # it depends on the layer: the buffers above never move, and a call
+        # then costs the host no tensor indexing.
+        def rows(t):
+            step = t.stride(0) * t.element_size()
+            return [t.data_ptr() + layer * step for layer in range(t.shape[0])]
+        self._bt = rows(self.block_tables)
+        self._q, self._k, self._v, self._out = rows(self.q), rows(self.k), rows(self.v), rows(self.out)
+        self._ctx = self.context_lens.data_ptr()
+        self._ws = self.workspace.data_ptr()
+        self._order_ptr = self.seq_order.data_ptr()
+        self._cos, self._sin = self.rope_cos.data_ptr(), self.rope_sin.data_ptr()
 
     @property
     def splits(self) -> int:
@@ -90,52 +102,52 @@ class DecodeBatch:
         self.context_lens.copy_(torch.from_numpy(self.context_lens_host))
 
     def _stream(self, stream):
+        if stream is not None:
+            return stream
         import torch
-        return stream if stream is not None else torch.cuda.current_stream(self.device)
+        return torch.cuda.current_stream(self.device)
 
     def order(self, stream=None) -> None:
         """Rank the sequences once for this step's attention calls (longest
         first); every later attention call of this batch starts them in that
         order."""
-        _lib.paged_decode_attn_order(self.context_lens, self.num_seqs, self.max_context_len,
-                                     self.seq_order, self._stream(stream))
+        _lib.paged_decode_attn_order(self._ctx, self.num_seqs, self.max_context_len,
+                                     self._order_ptr, self._stream(stream))
         self.ordered = True
 
     def _order(self):
-        return self.seq_order if self.ordered else None
+        return self._order_ptr if self.ordered else None
 
     def append(self, layer: int, stream=None) -> None:
         _lib.paged_kv_append(
-            self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
-            self.num_seqs, self.q[layer], Q_ROW, self.k[layer], KV_ROW, self.v[layer], KV_ROW,
-            self.rope_cos, self.rope_sin, self.max_pos, self._stream(stream))
+            self.pool, self._bt[layer], self.bt_stride, self._ctx, self.num_seqs,
+            self._q[layer], Q_ROW, self._k[layer], KV_ROW, self._v[layer], KV_ROW,
+            self._cos, self._sin, self.max_pos, self._stream(stream))
 
     def attn(self, layer: int, stream=None) -> None:
         _lib.paged_decode_attn(
-            self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
-            self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
-            seq_order=self._order())
+            self.pool, self._bt[layer], self.bt_stride, self._ctx, self.num_seqs,
+            self.max_context_len, self._q[layer], Q_ROW, self.scale, self._out[layer], Q_ROW,
+            self._ws, self.ws_bytes, self._stream(stream), seq_order=self._order())
 
     def attn_split(self, layer: int, stream=None) -> None:
         _lib.paged_decode_attn_split(
-            self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
-            self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
-            seq_order=self._order())
+            self.pool, self._bt[layer], self.bt_stride, self._ctx, self.num_seqs,
+            self.max_context_len, self._q[layer], Q_ROW, self.scale, self._out[layer], Q_ROW,
+            self._ws, self.ws_bytes, self._stream(stream), seq_order=self._order())
 
     def attn_combine(self, layer: int, stream=None) -> None:
         _lib.paged_decode_attn_combine(
-            self.context_lens, self.num_seqs, self.max_context_len, self.out[layer], Q_ROW,
-            self.workspace, self.ws_bytes, self._stream(stream))
+            self._ctx, self.num_seqs, self.max_context_len, self._out[layer], Q_ROW,
+            self._ws, self.ws_bytes, self._stream(stream))
 
     def append_attn(self, layer: int, stream=None) -> None:
         """The fused append + attention of one layer (q is left unrotated)."""
         _lib.paged_kv_append_decode_attn(
-            self.pool, self.block_tables[layer], self.bt_stride, self.context_lens,
-            self.num_seqs, self.max_context_len, self.q[layer], Q_ROW, self.k[layer], KV_ROW,
-            self.v[layer], KV_ROW, self.rope_cos, self.rope_sin, self.max_pos, self.scale,
-            self.out[layer], Q_ROW, self.workspace, self.ws_bytes, self._stream(stream),
+            self.pool, self._bt[layer], self.bt_stride, self._ctx, self.num_seqs,
+            self.max_context_len, self._q[layer], Q_ROW, self._k[layer], KV_ROW,
+            self._v[layer], KV_ROW, self._cos, self._sin, self.max_pos, self.scale,
+            self._out[layer], Q_ROW, self._ws, self.ws_bytes, self._stream(stream),
             seq_order=self._order())
 
     def step(self, stream=None) -> None:
