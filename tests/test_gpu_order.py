@@ -135,3 +135,39 @@ def test_order_changes_no_bit(torch_gpu, rope, how):
         assert torch.equal(out.view(torch.int32), out0.view(torch.int32)), (how, name)
         assert torch.equal(pool, pool0), (how, name)
     assert np.array_equal(ranked.cpu().numpy(), host_rank(spec.ctx, spec.ctx.max()))
+
+
+def test_issue_priority_changes_no_bit(torch_gpu, rope):
+    """Waves take their issue priority from their pages left only in launches
+    of at most two rounds of resident workgroups.  The same 64 sequences, alone
+    (512 workgroups: priority on) and as the first rows of a 1,024-sequence
+    batch (8,192 workgroups: priority off), must give the same output bits,
+    for the plain and the fused call."""
+    torch = torch_gpu
+    from paged_kv_cache_172_amd.runner import DecodeBatch
+    rng = np.random.default_rng(990)
+    lens = rng.integers(1, 300, 1024)
+    lens[::97] = 2048
+    spec = wl.make_spec(lens, 1, seed=990)
+    pool = wl.make_device_pool(spec)
+    q0, k0, v0 = wl.draw_new_tokens(spec)
+    big = DecodeBatch(pool, spec.block_tables, spec.ctx, q0, k0, v0, rope=rope, max_context_len=2048)
+    small = DecodeBatch(big.pool_pages, spec.block_tables[:, :64], spec.ctx[:64], q0[:, :64],
+                        k0[:, :64], v0[:, :64], rope=rope, max_context_len=2048)
+    assert big.pool_pages.data_ptr() == small.pool_pages.data_ptr()
+    assert big.splits == small.splits == 1
+    # the fused call first: it writes each new token's K/V row, which the
+    # device pool leaves NaN until then
+    for how in ("fused", "attn"):
+        say(f"[priority] {how}: B=1024 against its first 64 sequences")
+        for b in (big, small):
+            b.out.fill_(float("nan"))
+            if how == "attn":
+                b.attn(0)
+            else:
+                b.append_attn(0)
+        torch.cuda.synchronize()
+        got_big = big.out[0, :64].view(torch.int32)
+        got_small = small.out[0].view(torch.int32)
+        assert torch.equal(got_big, got_small), how
+        assert torch.isfinite(small.out[0]).all(), how
