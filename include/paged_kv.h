@@ -203,11 +203,17 @@ int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
  * sequence has its own attention length).  When a launch has more
  * workgroups than the GPU holds at once, they start in rank order, and a
  * long sequence that starts late sets the end of the launch; started
- * longest first, the long ones overlap the short ones.  Writes
- * seq_order[r] = the sequence of rank r, by descending page count
- * ceil(min(context_lens[s], max_context_len) / 16), ties in batch order --
- * a permutation of [0, num_seqs), computed on the device by one small
- * launch.  Lengths are the same for every layer of a decode step, so one
+ * longest first, the long ones overlap the short ones.  The sequences are
+ * sorted by descending page count ceil(min(context_lens[s],
+ * max_context_len) / 16), ties in batch order; sorted rank r then starts
+ * at position p(r), and seq_order[p(r)] = that sequence.  With R =
+ * paged_decode_attn_order_round() (the sequences whose workgroups start
+ * together) and num_seqs >= R >= 2, p reverses the second half of the
+ * first R ranks: p(r) = R/2 + (R - 1 - r) for R/2 <= r < R, else p(r) = r.
+ * The CUs that take the longest sequences of that first round then also
+ * take its shortest, so each CU's first workgroups carry about the same
+ * total pages.  A permutation of [0, num_seqs), computed on the device by
+ * one small launch.  Lengths are the same for every layer of a decode step, so one
  * call per step serves all its layers' attention calls (pass seq_order to
  * them).  The attention follows the order only when its workgroups exceed
  * what the GPU holds at once; the order never changes a result bit.
@@ -216,6 +222,14 @@ int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
  * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
  * [1, 2048]), HIP.  num_seqs == 0: no-op.
  */
+/*
+ * The round length R that paged_decode_attn_order uses on the current
+ * device: the sequences whose attention workgroups (one per KV head, single
+ * split) the device holds at once.  0 when it cannot be determined (the
+ * order is then the plain sorted order).
+ */
+int32_t paged_decode_attn_order_round(void);
+
 int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, int32_t* seq_order, void* stream);
 

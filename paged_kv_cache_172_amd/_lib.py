@@ -31,6 +31,7 @@ EXPORTED = (
     "paged_decode_attn_workspace_size",
     "paged_decode_attn_workspace_init",
     "paged_decode_attn_order",
+    "paged_decode_attn_order_round",
     "paged_decode_attn",
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
@@ -130,6 +131,7 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_workspace_size": ([i32, i32], ctypes.c_size_t),
         "paged_decode_attn_workspace_init": ([P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_order": ([P, i32, i32, P, P], ctypes.c_int),
+        "paged_decode_attn_order_round": ([], i32),
         "paged_decode_attn": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
                                ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_split": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
@@ -245,6 +247,10 @@ def paged_decode_attn_order(context_lens, num_seqs, max_context_len, seq_order,
     _check(load().paged_decode_attn_order(_p(context_lens), int(num_seqs), int(max_context_len),
                                           _p(seq_order), _stream(stream)),
            "paged_decode_attn_order")
+
+
+def paged_decode_attn_order_round() -> int:
+    return int(load().paged_decode_attn_order_round())
 
 
 def _attn_args(pool, block_table, bt_stride, context_lens, seq_order, num_seqs, max_context_len,

@@ -335,6 +335,8 @@ int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
                                         static_cast<hipStream_t>(stream)));
 }
 
+int32_t paged_decode_attn_order_round(void) { return pkv::resident_seqs(); }
+
 int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
     if (workspace_bytes == 0) return PKV_OK;
     if (!workspace) return PKV_ERR_INVALID_ARG;

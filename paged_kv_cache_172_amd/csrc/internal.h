@@ -149,6 +149,9 @@ hipError_t launch_order(const int32_t* context_lens, int32_t num_seqs, int32_t m
 // Attention workgroups the current device holds at once (looked up once per
 // device); INT64_MAX when the query fails.
 int64_t resident_workgroups();
+// Sequences whose single-split workgroups (one per KV head) the current
+// device holds at once: resident_workgroups() / 8, or 0 when unknown.
+int32_t resident_seqs();
 
 // The library's fixed device scratch (for callers that cannot allocate):
 // its size, and its address on the current device (looked up, and its

@@ -1041,8 +1041,20 @@ __device__ __forceinline__ int page_bin(const int32_t* ctx, int s, int max_conte
     return n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
 }
 
+// The position at which sorted rank r starts.  The first `round_len` ranks
+// start together (one round of resident workgroups); within it the second
+// half is reversed, so that the CUs which take the longest sequences in the
+// first half take the shortest of the round in the second, and each CU's
+// first workgroups carry about the same total pages.  Identity beyond the
+// round, or when round_len is 0 or the batch is smaller than a round.
+__device__ __forceinline__ int order_position(int r, int num_seqs, int round_len) {
+    if (round_len < 2 || num_seqs < round_len) return r;
+    const int half = round_len / 2;
+    return r >= half && r < round_len ? half + (round_len - 1 - r) : r;
+}
+
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx, int num_seqs, int max_context_len,
-                                                              int32_t* order) {
+                                                              int round_len, int32_t* order) {
     __shared__ int start[kOrderBins];                 // first rank of each count, this round
     __shared__ int wave_count[kOrderWaves][kOrderBins];
     const int tid = threadIdx.x;
@@ -1090,7 +1102,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx
         if (valid) {
             int pre = 0;
             for (int v = 0; v < wv; ++v) pre += wave_count[v][key];
-            order[start[key] + pre + lower] = s;
+            order[order_position(start[key] + pre + lower, num_seqs, round_len)] = s;
         }
         __syncthreads();
         for (int b = tid; b < kOrderBins; b += kOrderThreads) {
@@ -1127,8 +1139,15 @@ size_t scratch_bytes() { return kScratchBytes; }
 hipError_t launch_order(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                         int32_t* seq_order, hipStream_t stream) {
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, context_lens, num_seqs,
-                       max_context_len, seq_order);
+                       max_context_len, resident_seqs(), seq_order);
     return hipGetLastError();
+}
+
+int32_t resident_seqs() {
+    const int64_t wgs = resident_workgroups();
+    if (wgs == INT64_MAX) return 0;
+    const int64_t seqs = wgs / kKVHeads;
+    return seqs > INT32_MAX ? 0 : (int32_t)seqs;
 }
 
 int64_t resident_workgroups() {

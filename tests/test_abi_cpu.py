@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     assert set(names) == set(_lib.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -347,3 +347,14 @@ def test_copy_pages_rejects(lib):
         raise AssertionError("misaligned pool accepted")
     except pkv.PagedKVError as e:
         assert e.status == pkv.PKV_ERR_ALIGNMENT
+
+
+def test_order_round_without_gpu(lib):
+    """The round query needs a device; with none it reports 0 (plain sorted
+    order) rather than failing."""
+    import torch
+    r = pkv.paged_decode_attn_order_round()
+    if not torch.cuda.is_available():
+        assert r == 0
+    else:
+        assert r >= 0

@@ -3,7 +3,9 @@ the attention calls that follow it.
 
 The ranking is index work, so the bar is bit-exact: seq_order must equal the
 stable descending sort of the page counts ceil(min(ctx, max_context_len)/16)
-(numpy's stable argsort on the host, ties in batch order).  The order only
+(numpy's stable argsort on the host, ties in batch order), with the second
+half of the first round of R sequences reversed when the batch holds a whole
+round (R from paged_decode_attn_order_round).  The order only
 decides which workgroups start first, so every attention call (plain, split,
 fused, allocation-free) must give the same output and pool bits with and
 without it, on batches whose grid exceeds what the GPU holds at once (so the
@@ -35,10 +37,17 @@ def rope():
     return rope_table_host()
 
 
-def host_rank(ctx, max_context_len):
+def host_rank(ctx, max_context_len, round_len=0):
+    """The stable descending sort of the page counts; then, when the batch
+    holds a whole first round of round_len sequences, the second half of
+    that round reversed (sorted rank r starts at position p(r))."""
     n = np.minimum(np.asarray(ctx, np.int64), max_context_len)
     pages = np.where(n > 0, -(-n // 16), 0)
-    return np.argsort(-pages, kind="stable").astype(np.int32)
+    ranked = np.argsort(-pages, kind="stable").astype(np.int32)
+    if round_len >= 2 and ranked.size >= round_len:
+        half = round_len // 2
+        ranked[half:round_len] = ranked[half:round_len][::-1].copy()
+    return ranked
 
 
 ORDER_CASES = {
@@ -47,6 +56,8 @@ ORDER_CASES = {
     "two_rounds_1025": ("rand1025", 2048),
     "many_5000": ("rand5000", 2048),
     "all_equal_300": ([2048] * 300, 2048),
+    "one_round_128": ("rand128", 2048),
+    "one_short_of_a_round_127": ("rand127", 2048),
     "clamped_and_empty": ([0, -3, 5000, 2048, 17, 16, 1, 0, 3000, 33] * 7, 700),
 }
 
@@ -66,8 +77,10 @@ def test_order_is_the_stable_descending_sort(torch_gpu, name):
     pkv.paged_decode_attn_order(dev_ctx, ctx.size, mcl, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    want = host_rank(ctx, mcl)
-    say(f"[order] {name}: B={ctx.size}")
+    R = pkv.paged_decode_attn_order_round()
+    assert R >= 2 and R % 2 == 0, R
+    want = host_rank(ctx, mcl, R)
+    say(f"[order] {name}: B={ctx.size}, round {R}")
     assert np.array_equal(got, want), (name, got[:16], want[:16])
 
 
@@ -134,7 +147,8 @@ def test_order_changes_no_bit(torch_gpu, rope, how):
     for name, (out, pool) in results.items():
         assert torch.equal(out.view(torch.int32), out0.view(torch.int32)), (how, name)
         assert torch.equal(pool, pool0), (how, name)
-    assert np.array_equal(ranked.cpu().numpy(), host_rank(spec.ctx, spec.ctx.max()))
+    assert np.array_equal(ranked.cpu().numpy(),
+                          host_rank(spec.ctx, spec.ctx.max(), pkv.paged_decode_attn_order_round()))
 
 
 def test_issue_priority_changes_no_bit(torch_gpu, rope):
