@@ -749,9 +749,10 @@ void attn_split_kernel(AttnParams p) {
     const uint32_t rest = wg / kKVHeads;
     const int rank = (int)(rest % (uint32_t)p.num_seqs);
     const int ci = (int)(rest / (uint32_t)p.num_seqs);
-    // The sequence of this rank: the caller's order when given (started in
-    // that order, so the longest sequences do not start last), else batch
-    // order.  An entry outside [0, num_seqs) falls back to the rank itself.
+    // The sequence started at this position: the caller's order when given
+    // (paged_decode_attn_order: the longest sequences do not start last, and
+    // each CU's first workgroups carry about the same pages), else batch
+    // order.  An entry outside [0, num_seqs) falls back to the position itself.
     int s = rank;
     if (p.seq_order) {
         const int o = uniform(p.seq_order[rank]);
@@ -1030,6 +1031,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // the start of its count's range, plus its count's members in earlier
 // rounds, in earlier waves of this round, and in lower lanes of its own wave
 // (lanes with the same count found with one ballot per bit of the count).
+// The sorted rank then maps to the position the sequence starts at
+// (order_position: the first round of resident workgroups paired across CUs).
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderBins = kMaxContext / kPageTokens + 1;   // page counts 0..128
