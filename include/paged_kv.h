@@ -205,15 +205,18 @@ int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
  * long sequence that starts late sets the end of the launch; started
  * longest first, the long ones overlap the short ones.  The sequences are
  * sorted by descending page count ceil(min(context_lens[s],
- * max_context_len) / 16), ties in batch order; sorted rank r then starts
- * at position p(r), and seq_order[p(r)] = that sequence.  With R =
- * paged_decode_attn_order_round() (the sequences whose workgroups start
- * together) and num_seqs >= R >= 2, p reverses the second half of the
- * first R ranks: p(r) = R/2 + (R - 1 - r) for R/2 <= r < R, else p(r) = r.
- * The CUs that take the longest sequences of that first round then also
- * take its shortest, so each CU's first workgroups carry about the same
- * total pages.  A permutation of [0, num_seqs), computed on the device by
- * one small launch.  Lengths are the same for every layer of a decode step, so one
+ * max_context_len) / 16), ties in batch order; sorted rank r (0 = most
+ * pages) then starts at position p(r), and seq_order[p(r)] = that sequence.
+ * With R = paged_decode_attn_order_round() (the sequences whose workgroups
+ * start together), P = R/4 and B = num_seqs >= 4P >= 4:
+ *   r < 3P:          p = P + (2P - 1 - r) for P <= r < 2P, else p = r
+ *                    (the 3P longest, the middle quarter reversed);
+ *   r >= B - P:      p = 3P + (B - 1 - r)  (the P shortest, shortest first);
+ *   otherwise:       p = r + P              (the rest, longest first).
+ * Else p(r) = r.  The CUs that take the longest sequences in one slot round
+ * take shorter ones in the next, and the shortest sequences finish within
+ * the first round and hand their slots on.  A permutation of
+ * [0, num_seqs), computed on the device by one small launch.  Lengths are the same for every layer of a decode step, so one
  * call per step serves all its layers' attention calls (pass seq_order to
  * them).  The attention follows the order only when its workgroups exceed
  * what the GPU holds at once; the order never changes a result bit.

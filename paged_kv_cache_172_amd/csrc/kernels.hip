@@ -1032,7 +1032,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 // rounds, in earlier waves of this round, and in lower lanes of its own wave
 // (lanes with the same count found with one ballot per bit of the count).
 // The sorted rank then maps to the position the sequence starts at
-// (order_position: the first round of resident workgroups paired across CUs).
+// (order_position: the first round of resident workgroups balanced across
+// CUs).
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderBins = kMaxContext / kPageTokens + 1;   // page counts 0..128
@@ -1044,16 +1045,24 @@ __device__ __forceinline__ int page_bin(const int32_t* ctx, int s, int max_conte
     return n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
 }
 
-// The position at which sorted rank r starts.  The first `round_len` ranks
-// start together (one round of resident workgroups); within it the second
-// half is reversed, so that the CUs which take the longest sequences in the
-// first half take the shortest of the round in the second, and each CU's
-// first workgroups carry about the same total pages.  Identity beyond the
-// round, or when round_len is 0 or the batch is smaller than a round.
+// The position at which sorted rank r (0 = most pages) starts.  The first
+// `round_len` = R positions start together, one round of resident
+// workgroups; the dispatcher deals them to the CUs in R/4-position slot
+// rounds (one position per CU of an XCD).  With P = R/4: positions [0, 3P)
+// take the 3P longest sequences, the middle slot round reversed, so that the
+// CUs which take the longest in one round take the shorter in the next;
+// positions [3P, 4P) take the P shortest, shortest first, which finish within
+// the launch's ramp and hand their slots on; the rest follow, longest first.
+// Identity when R < 4 or the batch is smaller than a round.
 __device__ __forceinline__ int order_position(int r, int num_seqs, int round_len) {
-    if (round_len < 2 || num_seqs < round_len) return r;
-    const int half = round_len / 2;
-    return r >= half && r < round_len ? half + (round_len - 1 - r) : r;
+    const int P = round_len / 4;
+    if (P < 1 || num_seqs < 4 * P) return r;
+    if (r < 3 * P) {
+        const int slot = r / P, k = r - slot * P;
+        return slot == 1 ? P + (P - 1 - k) : r;
+    }
+    if (r >= num_seqs - P) return 3 * P + (num_seqs - 1 - r);
+    return r + P;
 }
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx, int num_seqs, int max_context_len,

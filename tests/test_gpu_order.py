@@ -3,9 +3,9 @@ the attention calls that follow it.
 
 The ranking is index work, so the bar is bit-exact: seq_order must equal the
 stable descending sort of the page counts ceil(min(ctx, max_context_len)/16)
-(numpy's stable argsort on the host, ties in batch order), with the second
-half of the first round of R sequences reversed when the batch holds a whole
-round (R from paged_decode_attn_order_round).  The order only
+(numpy's stable argsort on the host, ties in batch order), placed by the
+documented start positions when the batch holds a whole first round of R
+sequences (R from paged_decode_attn_order_round).  The order only
 decides which workgroups start first, so every attention call (plain, split,
 fused, allocation-free) must give the same output and pool bits with and
 without it, on batches whose grid exceeds what the GPU holds at once (so the
@@ -38,16 +38,21 @@ def rope():
 
 
 def host_rank(ctx, max_context_len, round_len=0):
-    """The stable descending sort of the page counts; then, when the batch
-    holds a whole first round of round_len sequences, the second half of
-    that round reversed (sorted rank r starts at position p(r))."""
+    """The stable descending sort of the page counts, then each sorted rank
+    placed at its start position: with P = round_len // 4 and a batch of at
+    least 4P sequences, the 3P longest first with the middle quarter of them
+    reversed, then the P shortest (shortest first), then the rest longest
+    first."""
     n = np.minimum(np.asarray(ctx, np.int64), max_context_len)
     pages = np.where(n > 0, -(-n // 16), 0)
     ranked = np.argsort(-pages, kind="stable").astype(np.int32)
-    if round_len >= 2 and ranked.size >= round_len:
-        half = round_len // 2
-        ranked[half:round_len] = ranked[half:round_len][::-1].copy()
-    return ranked
+    B, P = ranked.size, round_len // 4
+    if P < 1 or B < 4 * P:
+        return ranked
+    first = ranked[:3 * P].copy()
+    first[P:2 * P] = first[P:2 * P][::-1].copy()
+    shortest = ranked[B - P:][::-1]
+    return np.concatenate([first, shortest, ranked[3 * P:B - P]]).astype(np.int32)
 
 
 ORDER_CASES = {
@@ -58,6 +63,7 @@ ORDER_CASES = {
     "all_equal_300": ([2048] * 300, 2048),
     "one_round_128": ("rand128", 2048),
     "one_short_of_a_round_127": ("rand127", 2048),
+    "round_and_a_quarter_160": ("rand160", 2048),
     "clamped_and_empty": ([0, -3, 5000, 2048, 17, 16, 1, 0, 3000, 33] * 7, 700),
 }
 
