@@ -761,6 +761,13 @@ void attn_split_kernel(AttnParams p) {
     const int t = lane & 15;   // token slot of this lane (the MFMA column)
     const int c4 = lane >> 4;  // dims 8*c4..8*c4+7 and 32+8*c4..32+8*c4+7 (the MFMA k slice)
 
+    if constexpr (kFused) {
+        // The arguments the fused prologue reads, held in scalar registers
+        // from here: their loads join the first batch instead of following
+        // one another after the length arrives.
+        asm volatile("" ::"s"(p.q), "s"(p.q_stride), "s"(p.k_new), "s"(p.k_stride), "s"(p.v_new),
+                     "s"(p.v_stride), "s"(p.rope_cos), "s"(p.rope_sin), "s"(p.max_pos));
+    }
     // Independent loads first: the table row (first 128 entries, one per
     // lane in two registers), q of the 4 query heads, and the length.
     const int32_t* bt_row = p.block_table + (int64_t)s * p.bt_stride;
@@ -770,7 +777,20 @@ void attn_split_kernel(AttnParams p) {
     const int32_t tbl1 = lane + 64 < bt_w ? bt_row[lane + 64] : 0;
     QRegs q;
     const uint16_t* qrow = p.q + (int64_t)s * p.q_stride + (kGroup * g) * kHeadDim;
-    if constexpr (!kFused) {
+    // Fused: the new rows of the append's 48 row tasks, one per lane (lanes
+    // past 47 repeat the last one): 4 q heads, the new K and V of KV head g.
+    // They do not depend on the length, so they are requested with q's.
+    const int task = kFused ? min(lane, kRotTasks - 1) : 0;
+    const int row = task >> 3;
+    const int i0 = (task & 7) * 4;
+    uint2 x1 = make_uint2(0, 0), x2 = make_uint2(0, 0);
+    if constexpr (kFused) {
+        const uint16_t* src = row < kGroup ? qrow + row * kHeadDim
+                            : row == kGroup ? p.k_new + (int64_t)s * p.k_stride + g * kHeadDim
+                                            : p.v_new + (int64_t)s * p.v_stride + g * kHeadDim;
+        x1 = *reinterpret_cast<const uint2*>(src + i0);
+        x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
+    } else {
         const uint16_t* qh = qrow + (lane & 3) * kHeadDim + c4 * 8;
         q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qh));
         q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qh + 32));
@@ -843,17 +863,9 @@ void attn_split_kernel(AttnParams p) {
     cx.new_k = rot + kGroup * 32;
     cx.new_v = rot + (kGroup + 1) * 32;
     if constexpr (kFused) {
-        // Fused append, part 1: the 48 row tasks, one per lane (lanes past
-        // 47 repeat the last one).  Their inputs are requested before the
-        // first pages and the rotation runs while those are in flight.
-        const int task = min(lane, kRotTasks - 1);
-        const int row = task >> 3;
-        const int i0 = (task & 7) * 4;
-        const uint16_t* src = row < kGroup ? qrow + row * kHeadDim
-                            : row == kGroup ? p.k_new + (int64_t)s * p.k_stride + g * kHeadDim
-                                            : p.v_new + (int64_t)s * p.v_stride + g * kHeadDim;
-        uint2 x1 = *reinterpret_cast<const uint2*>(src + i0);
-        uint2 x2 = *reinterpret_cast<const uint2*>(src + i0 + 32);
+        // Fused append, part 1: the row tasks' RoPE rows (at the token's
+        // position) are requested before the first pages, and the rotation
+        // runs while those are in flight.
         const int64_t trow = (int64_t)(rotate ? pos : 0) * 32 + i0;
         const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + trow);
         const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + trow);
