@@ -129,12 +129,14 @@ def time_prefill(torch, pkv, stream, rope_cos, rope_sin, reps: int):
 def time_continuous_batching(torch, stream, rope, reps: int):
     """The continuous-batching mix: 256 sequences x 16 layers, context lengths
     log-uniform in 16..2,048, 16 of them opening a page this step (lazy page
-    step first).  The fused step, timed per layer, in three ways: the batch as
+    step first).  The fused step, timed per layer, in four ways: the batch as
     given, ranked once per step by the library (paged_decode_attn_order, its
     launch inside the timed step) and followed by every layer's call
     (``given_order``); the batch as given with no order
-    (``given_order_unranked``); and sorted longest-first by the caller
-    (``longest_first``).  The kernels' results do not depend on the order;
+    (``given_order_unranked``); sorted longest-first by the caller
+    (``longest_first``); and laid out by the caller in the library's start
+    order computed on the host (paged_decode_attn_order_host,
+    ``host_order``).  The kernels' results do not depend on the order;
     with 2,048 (sequence, KV head) workgroups, twice what the GPU holds at
     once, the order sets the tail."""
     from paged_kv_cache_172_amd import pages as pg, workload as wl
@@ -151,8 +153,11 @@ def time_continuous_batching(torch, stream, rope, reps: int):
                        f"(sum {int(spec.ctx.sum())} tokens per layer)",
            "kv_bytes_per_layer": int(kv_layer)}
     longest = np.argsort(-spec.ctx, kind="stable")
+    from paged_kv_cache_172_amd import _lib
+    host_order = _lib.paged_decode_attn_order_host(spec.ctx, wl.MAX_CONTEXT,
+                                                   _lib.paged_decode_attn_order_round())
     for name, perm, ranked in (("given_order", None, True), ("given_order_unranked", None, False),
-                               ("longest_first", longest, False)):
+                               ("longest_first", longest, False), ("host_order", host_order, False)):
         if perm is None:
             args = (bt, spec.ctx, q0, k0, v0)
         else:

@@ -233,6 +233,23 @@ int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
  */
 int32_t paged_decode_attn_order_round(void);
 
+/*
+ * The same start order computed on the host, for callers that lay out the
+ * batch themselves (a serving host knows its lengths): placing sequence
+ * seq_order[p] at batch row p gives the attention calls that order with no
+ * seq_order argument, so their workgroups need not look it up.  Pass
+ * round_len = paged_decode_attn_order_round() for the current device (0
+ * gives the plain sorted order).  Equal, entry for entry, to what
+ * paged_decode_attn_order writes for the same lengths on a device whose
+ * round length is round_len.
+ *   context_lens  (host) int32 [num_seqs]
+ *   seq_order     (host) int32 [num_seqs], written
+ * Errors: INVALID_ARG (null pointer, num_seqs < 0, round_len < 0,
+ * max_context_len outside [1, 2048]).  num_seqs == 0: no-op.  No HIP call.
+ */
+int paged_decode_attn_order_host(const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, int32_t round_len, int32_t* seq_order);
+
 int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, int32_t* seq_order, void* stream);
 

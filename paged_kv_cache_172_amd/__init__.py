@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     paged_decode_attn_num_splits,
     paged_decode_attn_order,
     paged_decode_attn_order_round,
+    paged_decode_attn_order_host,
     paged_decode_attn_split,
     paged_decode_attn_workspace_init,
     paged_decode_attn_workspace_size,

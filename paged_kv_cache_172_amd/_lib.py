@@ -32,6 +32,7 @@ EXPORTED = (
     "paged_decode_attn_workspace_init",
     "paged_decode_attn_order",
     "paged_decode_attn_order_round",
+    "paged_decode_attn_order_host",
     "paged_decode_attn",
     "paged_decode_attn_split",
     "paged_decode_attn_combine",
@@ -132,6 +133,7 @@ def load(path: str = LIB_PATH):
         "paged_decode_attn_workspace_init": ([P, ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_order": ([P, i32, i32, P, P], ctypes.c_int),
         "paged_decode_attn_order_round": ([], i32),
+        "paged_decode_attn_order_host": ([P, i32, i32, i32, P], ctypes.c_int),
         "paged_decode_attn": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
                                ctypes.c_size_t, P], ctypes.c_int),
         "paged_decode_attn_split": ([PP, P, i64, P, P, i32, i32, P, i64, f32, P, i64, P,
@@ -251,6 +253,18 @@ def paged_decode_attn_order(context_lens, num_seqs, max_context_len, seq_order,
 
 def paged_decode_attn_order_round() -> int:
     return int(load().paged_decode_attn_order_round())
+
+
+def paged_decode_attn_order_host(context_lens, max_context_len, round_len):
+    """The start order on the host: context_lens is a host int32 array;
+    returns the int32 order array."""
+    import numpy as np
+    ctx = np.ascontiguousarray(context_lens, np.int32)
+    out = np.empty(ctx.size, np.int32)
+    _check(load().paged_decode_attn_order_host(ctx.ctypes.data, int(ctx.size), int(max_context_len),
+                                                int(round_len), out.ctypes.data),
+           "paged_decode_attn_order_host")
+    return out
 
 
 def _attn_args(pool, block_table, bt_stride, context_lens, seq_order, num_seqs, max_context_len,

@@ -337,6 +337,27 @@ int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
 
 int32_t paged_decode_attn_order_round(void) { return pkv::resident_seqs(); }
 
+int paged_decode_attn_order_host(const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                 int32_t round_len, int32_t* seq_order) {
+    if (num_seqs < 0 || round_len < 0) return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PKV_OK;
+    if (!context_lens || !seq_order || max_context_len < 1 || max_context_len > pkv::kMaxContext)
+        return PKV_ERR_INVALID_ARG;
+    // The same order as order_kernel: a stable counting sort by descending
+    // page count, then each sorted rank written at its start position.
+    constexpr int kBins = pkv::kMaxContext / pkv::kPageTokens + 1;
+    int64_t start[kBins + 1] = {};
+    for (int32_t s = 0; s < num_seqs; ++s)
+        ++start[kBins - 1 - pkv::order_page_count(context_lens[s], max_context_len) + 1];
+    for (int b = 1; b <= kBins; ++b) start[b] += start[b - 1];   // start[kBins-1-count]: first rank of count
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int bin = kBins - 1 - pkv::order_page_count(context_lens[s], max_context_len);
+        const int r = (int)start[bin]++;
+        seq_order[pkv::order_position(r, num_seqs, round_len)] = s;
+    }
+    return PKV_OK;
+}
+
 int paged_decode_attn_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
     if (workspace_bytes == 0) return PKV_OK;
     if (!workspace) return PKV_ERR_INVALID_ARG;

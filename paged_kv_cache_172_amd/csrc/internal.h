@@ -148,6 +148,31 @@ hipError_t launch_order(const int32_t* context_lens, int32_t num_seqs, int32_t m
                         int32_t* seq_order, hipStream_t stream);
 // Attention workgroups the current device holds at once (looked up once per
 // device); INT64_MAX when the query fails.
+// The position at which sorted rank r (0 = most pages) starts.  The first
+// `round_len` = R positions start together, one round of resident
+// workgroups; the dispatcher deals them to the CUs in R/4-position slot
+// rounds (one position per CU of an XCD).  With P = R/4: positions [0, 3P)
+// take the 3P longest sequences, the middle slot round reversed, so that the
+// CUs which take the longest in one round take the shorter in the next;
+// positions [3P, 4P) take the P shortest, shortest first, which finish within
+// the launch's ramp and hand their slots on; the rest follow, longest first.
+// Identity when R < 4 or the batch is smaller than a round.
+__host__ __device__ inline int order_position(int r, int num_seqs, int round_len) {
+    const int P = round_len / 4;
+    if (P < 1 || num_seqs < 4 * P) return r;
+    if (r < 3 * P) {
+        const int slot = r / P, k = r - slot * P;
+        return slot == 1 ? P + (P - 1 - k) : r;
+    }
+    if (r >= num_seqs - P) return 3 * P + (num_seqs - 1 - r);
+    return r + P;
+}
+// The page count the start order ranks by: ceil(min(ctx, max_context_len) / 16), 0 when ctx <= 0.
+__host__ __device__ inline int order_page_count(int32_t ctx, int32_t max_context_len) {
+    const int n = ctx < max_context_len ? ctx : max_context_len;
+    return n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
+}
+
 int64_t resident_workgroups();
 // Sequences whose single-split workgroups (one per KV head) the current
 // device holds at once: resident_workgroups() / 8, or 0 when unknown.

@@ -1052,29 +1052,7 @@ constexpr int kOrderBins = kMaxContext / kPageTokens + 1;   // page counts 0..12
 static_assert(kOrderBins <= 255, "counts fit 8 bits; 255 marks no sequence");
 
 __device__ __forceinline__ int page_bin(const int32_t* ctx, int s, int max_context_len) {
-    const int c = ctx[s];
-    const int n = c < max_context_len ? c : max_context_len;
-    return n > 0 ? (n + kPageTokens - 1) / kPageTokens : 0;
-}
-
-// The position at which sorted rank r (0 = most pages) starts.  The first
-// `round_len` = R positions start together, one round of resident
-// workgroups; the dispatcher deals them to the CUs in R/4-position slot
-// rounds (one position per CU of an XCD).  With P = R/4: positions [0, 3P)
-// take the 3P longest sequences, the middle slot round reversed, so that the
-// CUs which take the longest in one round take the shorter in the next;
-// positions [3P, 4P) take the P shortest, shortest first, which finish within
-// the launch's ramp and hand their slots on; the rest follow, longest first.
-// Identity when R < 4 or the batch is smaller than a round.
-__device__ __forceinline__ int order_position(int r, int num_seqs, int round_len) {
-    const int P = round_len / 4;
-    if (P < 1 || num_seqs < 4 * P) return r;
-    if (r < 3 * P) {
-        const int slot = r / P, k = r - slot * P;
-        return slot == 1 ? P + (P - 1 - k) : r;
-    }
-    if (r >= num_seqs - P) return 3 * P + (num_seqs - 1 - r);
-    return r + P;
+    return order_page_count(ctx[s], max_context_len);
 }
 
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx, int num_seqs, int max_context_len,
