@@ -199,33 +199,6 @@ int paged_kv_copy_pages(const paged_kv_pool* pool, const int32_t* src, const int
 int32_t paged_decode_attn_num_splits(int32_t num_seqs, int32_t max_context_len);
 
 /*
- * Start order of a decode batch whose lengths differ ([HN-batch]: each
- * sequence has its own attention length).  When a launch has more
- * workgroups than the GPU holds at once, they start in rank order, and a
- * long sequence that starts late sets the end of the launch; started
- * longest first, the long ones overlap the short ones.  The sequences are
- * sorted by descending page count ceil(min(context_lens[s],
- * max_context_len) / 16), ties in batch order; sorted rank r (0 = most
- * pages) then starts at position p(r), and seq_order[p(r)] = that sequence.
- * With R = paged_decode_attn_order_round() (the sequences whose workgroups
- * start together), P = R/4 and B = num_seqs >= 4P >= 4:
- *   r < 3P:          p = P + (2P - 1 - r) for P <= r < 2P, else p = r
- *                    (the 3P longest, the middle quarter reversed);
- *   r >= B - P:      p = 3P + (B - 1 - r)  (the P shortest, shortest first);
- *   otherwise:       p = r + P              (the rest, longest first).
- * Else p(r) = r.  The CUs that take the longest sequences in one slot round
- * take shorter ones in the next, and the shortest sequences finish within
- * the first round and hand their slots on.  A permutation of
- * [0, num_seqs), computed on the device by one small launch.  Lengths are the same for every layer of a decode step, so one
- * call per step serves all its layers' attention calls (pass seq_order to
- * them).  The attention follows the order only when its workgroups exceed
- * what the GPU holds at once; the order never changes a result bit.
- *   context_lens  (device) int32 [num_seqs]
- *   seq_order     (device) int32 [num_seqs], written
- * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
- * [1, 2048]), HIP.  num_seqs == 0: no-op.
- */
-/*
  * The round length R that paged_decode_attn_order uses on the current
  * device: the sequences whose attention workgroups (one per KV head, single
  * split) the device holds at once.  0 when it cannot be determined (the
@@ -250,6 +223,34 @@ int32_t paged_decode_attn_order_round(void);
 int paged_decode_attn_order_host(const int32_t* context_lens, int32_t num_seqs,
                                  int32_t max_context_len, int32_t round_len, int32_t* seq_order);
 
+/*
+ * Start order of a decode batch whose lengths differ ([HN-batch]: each
+ * sequence has its own attention length).  When a launch has more
+ * workgroups than the GPU holds at once, they start in rank order, and a
+ * long sequence that starts late sets the end of the launch; started
+ * longest first, the long ones overlap the short ones.  The sequences are
+ * sorted by descending page count ceil(min(context_lens[s],
+ * max_context_len) / 16), ties in batch order; sorted rank r (0 = most
+ * pages) then starts at position p(r), and seq_order[p(r)] = that sequence.
+ * With R = paged_decode_attn_order_round() (the sequences whose workgroups
+ * start together), P = R/4 and B = num_seqs >= 4P >= 4:
+ *   r < 3P:          p = P + (2P - 1 - r) for P <= r < 2P, else p = r
+ *                    (the 3P longest, the middle quarter reversed);
+ *   r >= B - P:      p = 3P + (B - 1 - r)  (the P shortest, shortest first);
+ *   otherwise:       p = r + P              (the rest, longest first).
+ * Else p(r) = r.  The CUs that take the longest sequences in one slot round
+ * take shorter ones in the next, and the shortest sequences finish within
+ * the first round and hand their slots on.  A permutation of
+ * [0, num_seqs), computed on the device by one small launch.  Lengths are
+ * the same for every layer of a decode step, so one call per step serves
+ * all its layers' attention calls (pass seq_order to them).  The attention
+ * follows the order only when its workgroups exceed what the GPU holds at
+ * once; the order never changes a result bit.
+ *   context_lens  (device) int32 [num_seqs]
+ *   seq_order     (device) int32 [num_seqs], written
+ * Errors: INVALID_ARG (null pointer, num_seqs < 0, max_context_len outside
+ * [1, 2048]), HIP.  num_seqs == 0: no-op.
+ */
 int paged_decode_attn_order(const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, int32_t* seq_order, void* stream);
 
