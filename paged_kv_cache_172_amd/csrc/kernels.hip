@@ -825,6 +825,11 @@ void attn_split_kernel(AttnParams p) {
     const uint32_t k_off = (uint32_t)((t * p.slot_stride + c4 * 8) * 2);
     const uint32_t v_off = (uint32_t)(((lane >> 2) * p.slot_stride + (lane & 3) * 8) * 2);
     const int32_t tile_bytes = (int32_t)((15 * p.slot_stride + kHeadDim) * 2);
+    // The sequence's last page holds 1..16 valid slots: its range ends after
+    // the last valid row, so the loads of the rows past it return zeros
+    // without reading memory (the mask leaves those slots out anyway).
+    const int last_rows = np > 0 ? n - (np - 1) * kPageTokens : kPageTokens;
+    const int32_t last_tile_bytes = (int32_t)(((last_rows - 1) * p.slot_stride + kHeadDim) * 2);
     const char* kpool = reinterpret_cast<const char*>(p.k_pool) + (int64_t)g * p.head_stride * 2;
     const char* vpool = reinterpret_cast<const char*>(p.v_pool) + (int64_t)g * p.head_stride * 2;
     const int64_t page_bytes = p.page_stride * 2;
@@ -839,7 +844,7 @@ void attn_split_kernel(AttnParams p) {
             bad_page |= live;
             phys = 0;
         }
-        const int32_t bytes = live ? tile_bytes : 0;
+        const int32_t bytes = live ? (j == np - 1 ? last_tile_bytes : tile_bytes) : 0;
         const int64_t off = (int64_t)phys * page_bytes;
         return load_page(tile_rsrc(kpool + off, bytes), tile_rsrc(vpool + off, bytes), k_off,
                          v_off);
