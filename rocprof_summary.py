@@ -16,7 +16,7 @@
         result is written where bench.py reads it, tagged with the hash of
         the kernel source it was measured on.
 
-    python rocprof_summary.py counters --kernel SUBSTR [--first N] F.csv [...]
+    python rocprof_summary.py counters --kernel SUBSTR [--first N] [--grid G] F.csv [...]
         Mean of every counter per dispatch of one kernel (any counters).
 """
 from __future__ import annotations
@@ -134,12 +134,12 @@ def traffic(a) -> dict:
     return res
 
 
-def counter_means(paths, kernel: str, first: int | None):
+def counter_means(paths, kernel: str, first: int | None, grid: int = 0):
     per = defaultdict(dict)   # counter -> {dispatch id: value}
     for path in paths:
         with open(path, newline="") as f:
             for r in csv.DictReader(f):
-                if kernel in r["Kernel_Name"]:
+                if kernel in r["Kernel_Name"] and (not grid or int(r["Grid_Size"]) == grid):
                     d = int(r["Dispatch_Id"])
                     per[r["Counter_Name"]][d] = per[r["Counter_Name"]].get(d, 0.0) + \
                         float(r["Counter_Value"])
@@ -167,6 +167,8 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("--kernel", required=True)
     c.add_argument("--first", type=int)
+    c.add_argument("--grid", type=int, default=0,
+                   help="only dispatches of this grid size in work-items (one workload)")
     c.add_argument("csv", nargs="+")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
@@ -177,7 +179,7 @@ def main(argv=None):
     elif a.cmd == "traffic":
         print(json.dumps(traffic(a), indent=1))
     else:
-        res = counter_means(a.csv, a.kernel, a.first)
+        res = counter_means(a.csv, a.kernel, a.first, a.grid)
         print("| counter | mean per dispatch | dispatches |")
         print("|---|---|---|")
         for name in sorted(res):
