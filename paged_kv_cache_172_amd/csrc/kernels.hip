@@ -867,35 +867,37 @@ void attn_split_kernel(AttnParams p) {
     cx.slot = pos & (kPageTokens - 1);
     cx.new_k = rot + kGroup * 32;
     cx.new_v = rot + (kGroup + 1) * 32;
-    if constexpr (kFused) {
-        // Fused append, part 1: the row tasks' RoPE rows (at the token's
-        // position) are requested before the first pages, and the rotation
-        // runs while those are in flight.
-        const int64_t trow = (int64_t)(rotate ? pos : 0) * 32 + i0;
-        const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + trow);
-        const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + trow);
-        // Empty chunks issue no-op loads, so every wave takes the same path.
-        ring_fill<0>(ring, pb, issue);
-        if (rotate && row <= kGroup) rope4(x1, x2, c, sn);
-        if (lane < kRotTasks) {
-            *reinterpret_cast<uint2*>(&rot[row * 32 + i0 / 2]) = x1;
-            *reinterpret_cast<uint2*>(&rot[row * 32 + 16 + i0 / 2]) = x2;
-        }
-
-        // Fused append, part 2: the wave's lanes take the rotated q rows
-        // (LDS ops of one wave complete in order; the fences keep the
-        // compiler from moving the reads above the writes).  When the new
-        // token lies inside the attended length, the page that holds it
-        // takes the token's K and V rows from LDS (consume_page).
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + c4 * 4]));
-        q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + 16 + c4 * 4]));
-        if (rotate && ctx == n) tok_page = np - 1;
-    }
-
     if (pb < pe) {
+        if constexpr (kFused) {
+            // Fused append, part 1: the row tasks' RoPE rows (at the token's
+            // position) are requested before the first pages, and the rotation
+            // runs while those are in flight.  A wave with an empty chunk
+            // skips all of it (it never uses q, and wave 0 of outer chunk 0,
+            // which stores the K/V row, always has pages when the token is
+            // rotated): in a batch of short sequences its loads and rotation
+            // would only compete with the waves that stream.
+            const int64_t trow = (int64_t)(rotate ? pos : 0) * 32 + i0;
+            const float4 c = *reinterpret_cast<const float4*>(p.rope_cos + trow);
+            const float4 sn = *reinterpret_cast<const float4*>(p.rope_sin + trow);
+            ring_fill<0>(ring, pb, issue);
+            if (rotate && row <= kGroup) rope4(x1, x2, c, sn);
+            if (lane < kRotTasks) {
+                *reinterpret_cast<uint2*>(&rot[row * 32 + i0 / 2]) = x1;
+                *reinterpret_cast<uint2*>(&rot[row * 32 + 16 + i0 / 2]) = x2;
+            }
+
+            // Fused append, part 2: the wave's lanes take the rotated q rows
+            // (LDS ops of one wave complete in order; the fences keep the
+            // compiler from moving the reads above the writes).  When the new
+            // token lies inside the attended length, the page that holds it
+            // takes the token's K and V rows from LDS (consume_page).
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            q.a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + c4 * 4]));
+            q.b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&rot[(lane & 3) * 32 + 16 + c4 * 4]));
+            if (rotate && ctx == n) tok_page = np - 1;
+        }
         if constexpr (!kFused) ring_fill<0>(ring, pb, issue);
         const float sl2 = p.scale_log2;
         int j = pb;
