@@ -696,9 +696,9 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 
 // Row tasks of the fused append: 6 rows (query heads 4g..4g+3 and the new
 // K of head g, rotated; the new V of head g, copied) x 8 groups of 4 pairs
-// (dims i0..i0+3 and i0+32..i0+35).  Every wave runs all 48 in its lanes
-// 0..47 and passes the rows to its other lanes through its own LDS rows, so
-// no wave waits for another.
+// (dims i0..i0+3 and i0+32..i0+35).  Every wave that has pages runs all 48
+// in its lanes 0..47 and passes the rows to its other lanes through its own
+// LDS rows, so no wave waits for another.
 constexpr int kRotRows = kGroup + 2;
 constexpr int kRotTasks = kRotRows * 8;
 static_assert(kRotTasks <= 64, "one task per lane");
