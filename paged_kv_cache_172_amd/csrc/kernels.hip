@@ -1046,7 +1046,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 //
 // One workgroup ranks the num_seqs sequences by descending page count
 // (stable: ties keep batch order), a counting sort over the 129 possible
-// counts.  Rounds of 1,024 sequences, one per thread: a thread's place is
+// counts: a histogram in LDS, its exclusive prefix (longest first) scanned
+// by one wave, then rounds of 1,024 sequences, one per thread: a thread's place is
 // the start of its count's range, plus its count's members in earlier
 // rounds, in earlier waves of this round, and in lower lanes of its own wave
 // (lanes with the same count found with one ballot per bit of the count).
@@ -1071,33 +1072,45 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* ctx
     const int wv = tid >> 6;
     for (int b = tid; b < kOrderBins; b += kOrderThreads) start[b] = 0;
     for (int i = tid; i < kOrderWaves * kOrderBins; i += kOrderThreads) (&wave_count[0][0])[i] = 0;
+    // The first round's counts stay in registers for the ranking below.
+    const int key0 = tid < num_seqs ? page_bin(ctx, tid, max_context_len) : 255;
     __syncthreads();
     // histogram (start[] doubles as the count of each bin)
-    for (int s = tid; s < num_seqs; s += kOrderThreads) atomicAdd(&start[page_bin(ctx, s, max_context_len)], 1);
-    // Exclusive prefix over the counts, longest first: an inclusive scan of
-    // the counts in descending-count order (position t holds count 128 - t),
-    // by doubling steps over 256 positions.
-    __shared__ int scan[256];
-    static_assert(kOrderBins <= 256, "one scan position per count");
+    if (key0 != 255) atomicAdd(&start[key0], 1);
+    for (int s = tid + kOrderThreads; s < num_seqs; s += kOrderThreads)
+        atomicAdd(&start[page_bin(ctx, s, max_context_len)], 1);
     __syncthreads();   // every count is in
-    if (tid < 256) scan[tid] = tid < kOrderBins ? start[kOrderBins - 1 - tid] : 0;
-    for (int off = 1; off < 256; off <<= 1) {
-        __syncthreads();
-        const int add = tid < 256 && tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        if (tid < 256) scan[tid] += add;
-    }
-    __syncthreads();
-    if (tid < kOrderBins) {
-        const int b = kOrderBins - 1 - tid;
-        start[b] = scan[tid] - start[b];
+    // Exclusive prefix over the counts, longest first, in one wave: lane l
+    // holds scan positions 4l..4l+3 (position t is the count 128 - t).
+    static_assert(kOrderBins <= 256, "four scan positions per lane");
+    if (wv == 0) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lane + i;
+            v[i] = t < kOrderBins ? start[kOrderBins - 1 - t] : 0;
+            sum += v[i];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lane + i;
+            if (t < kOrderBins) start[kOrderBins - 1 - t] = run;
+            run += v[i];
+        }
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int r0 = 0; r0 < num_seqs; r0 += kOrderThreads) {
         const int s = r0 + tid;
         const bool valid = s < num_seqs;
-        const int key = valid ? page_bin(ctx, s, max_context_len) : 255;
+        const int key = r0 == 0 ? key0 : valid ? page_bin(ctx, s, max_context_len) : 255;
         uint64_t same = ~0ull;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
